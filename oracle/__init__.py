@@ -1,0 +1,3 @@
+"""fp64 CPU oracle for LoopVQ (test infrastructure only; see loopvq_ref)."""
+from .loopvq_ref import *  # noqa: F401,F403
+from .loopvq_ref import NEAR_TIE_REL, NearestResult  # noqa: F401
