@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of LoopVQ decode attention (32K context) and of the encoder on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--copy-probe] [--skip-encode]
+
+One step = one quantised decode-attention call (split-K kernel + combine) of
+the long-context workload at one loop step, for all KV and query heads of a
+batch of 16 requests with 32768 cached tokens each; the loop step cycles
+t = 1..4 from step to step.  The cache it reads was built beforehand by the
+GPU encoder from synthetic loop-correlated keys and values.  The encoder is
+timed separately on the prefill of the 1.4B-layer workload (8 x 4096 tokens).
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+METRIC = "decode-attn cached tokens/s (all heads, 1 loop step) @32K ctx; encode vecs/s"
+DECODE_KERNEL = "decode_split_kernel"
+
+
+def _source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(sha: str):
+    """HBM bytes per launch from committed PMC counters, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_split_longctx32k_pmc.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def build_cache(cfg, lv, dims, layer_cb, layer_hsq, lens, bt_np, num_pages, seed, torch, synth):
+    """Encode every request's synthetic K/V (all blocks) into a fresh paged cache on the GPU."""
+    cache = torch.zeros((cfg.n_blocks, num_pages, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes),
+                        dtype=torch.uint8, device="cuda")
+    for b, n in enumerate(lens):
+        n = int(n)
+        if n == 0:
+            continue
+        xk, xv = synth.make_kv_torch(cfg, n, seed * 1000 + b)
+        slots = torch.from_numpy(synth.slot_mapping_for(bt_np, b, n, cfg.page_size)).cuda()
+        lv.loopvq_encode(dims, xk, xv, layer_cb, layer_hsq, slots, cache, n_blocks=cfg.n_blocks,
+                         block_stride_bytes=cache[0].numel())
+        del xk, xv
+    torch.cuda.synchronize()
+    return cache
+
+
+def bench_decode(args, torch, np, synth, lv):
+    cfg = synth.config_by_name("longctx32k")
+    lens = synth.make_seq_lens(cfg)
+    B = len(lens)
+    max_seq_len = int(lens.max())
+    bt_np, num_pages = synth.make_block_table(cfg, lens)
+    dims = lv.loopvq_dims.make(D=cfg.D, c=cfg.c, Tc=cfg.Tc, T=cfg.T, bits=cfg.bits, H_kv=cfg.H_kv,
+                               H_q=cfg.H_q, page_size=cfg.page_size, x_dtype=cfg.x_dtype,
+                               io_dtype=cfg.io_dtype)
+    cb = torch.from_numpy(synth.make_codebooks(cfg)).cuda()
+    slices, hsq = lv.loopvq_build_codebook_slices(dims, cb)
+    cache = build_cache(cfg, lv, dims, cb, hsq, lens, bt_np, num_pages, cfg.index, torch, synth)
+    rope = lv.loopvq_rope_table(max_seq_len, cfg.D, cfg.base).cuda()
+    bt = torch.from_numpy(bt_np).cuda()
+    seq = torch.from_numpy(lens.astype(np.int32)).cuda()
+    qs = [torch.from_numpy(synth.make_queries(cfg, B, t=t)).to(torch.bfloat16).cuda() for t in range(1, cfg.T + 1)]
+    out = torch.empty((B, cfg.H_q, cfg.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lv.loopvq_decode_workspace_bytes(dims, B, max_seq_len), dtype=torch.uint8, device="cuda")
+
+    def step(i, ev=None):
+        t = i % cfg.T + 1
+        if ev is not None:
+            ev[0].record()
+        lv.loopvq_decode_split(dims, t, qs[t - 1], cache[0], slices, rope, bt, seq, max_seq_len, ws)
+        if ev is not None:
+            ev[1].record()
+        lv.loopvq_decode_combine(dims, B, seq, max_seq_len, ws, out, lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    per_t = {}
+    for i, ms in enumerate(split_ms):
+        per_t.setdefault((args.warmup + i) % cfg.T + 1, []).append(ms)
+    ms_per_step = ms_total / args.steps
+    tokens = int(lens.sum())
+    value = tokens / (ms_per_step * 1e-3)
+    # algorithmic bytes of one split launch: two index rows per (token, KV head),
+    # one RoPE-table row per position, one block-table entry per page
+    index_bytes = tokens * cfg.H_kv * 2 * cfg.row_bytes
+    rope_bytes = max_seq_len * cfg.D * 4
+    bt_bytes = sum((int(n) + cfg.page_size - 1) // cfg.page_size for n in lens) * 4
+    algo = index_bytes + rope_bytes + bt_bytes
+    split_avg = float(np.mean(split_ms))
+    achieved = algo / (split_avg * 1e-3) / 1e9
+    sha = _source_sha()
+    traffic = _traffic_from_profile(sha)
+    res = dict(
+        value=value, ms_per_step=ms_per_step, wall_s=t_wall, cfg=cfg, lens=lens, max_seq_len=max_seq_len,
+        split_avg_ms=split_avg, combine_avg_ms=ms_per_step - split_avg,
+        per_t_tokens_per_s={str(t): tokens / (np.mean(v) * 1e-3) for t, v in sorted(per_t.items())},
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                  "kernel": DECODE_KERNEL, "algorithmic_bytes_per_launch": algo,
+                  "avg_launch_ms": round(split_avg, 5), "source_sha": sha},
+        cache=cache, bt_np=bt_np, cb=cb, qs=qs, dims=dims,
+    )
+    return res
+
+
+def bench_encode(args, torch, np, synth, lv):
+    cfg = synth.config_by_name("layer1p4b")
+    n_tok = cfg.encode_batch * cfg.encode_tokens
+    lens = np.full(cfg.encode_batch, cfg.encode_tokens)
+    bt_np, num_pages = synth.make_block_table(cfg, lens)
+    slots = torch.from_numpy(np.concatenate([synth.slot_mapping_for(bt_np, b, int(n), cfg.page_size)
+                                             for b, n in enumerate(lens)])).cuda()
+    dims = lv.loopvq_dims.make(D=cfg.D, c=cfg.c, Tc=cfg.Tc, T=cfg.T, bits=cfg.bits, H_kv=cfg.H_kv,
+                               H_q=cfg.H_q, page_size=cfg.page_size, x_dtype=cfg.x_dtype,
+                               io_dtype=cfg.io_dtype)
+    cb = torch.from_numpy(synth.make_codebooks(cfg)).cuda()
+    _, hsq = lv.loopvq_build_codebook_slices(dims, cb)
+    xk, xv = synth.make_kv_torch(cfg, n_tok, 77)
+    cache = torch.zeros((num_pages, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+    reps = max(3, args.steps // 4)
+    for _ in range(2):
+        lv.loopvq_encode(dims, xk, xv, cb, hsq, slots, cache)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lv.loopvq_encode(dims, xk, xv, cb, hsq, slots, cache)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    vecs = n_tok * cfg.H_kv * 2 * cfg.n_groups * cfg.n_blocks
+    flops = vecs * 2 * cfg.G * cfg.K
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"metric": "encode vecs/s", "value": vecs / (ms * 1e-3), "unit": "coupled vectors/s",
+            "ms_per_call": ms, "workload": f"{cfg.name}: prefill encode of {cfg.encode_batch} x "
+            f"{cfg.encode_tokens} tokens, H_kv={cfg.H_kv}, D={cfg.D}, c={cfg.c}, Tc={cfg.Tc}, K={cfg.K}",
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "encode_kernel", "algorithmic_flops_per_launch": flops}}
+
+
+def cpu_baseline(np, synth, dec, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the same decode workload, one core."""
+    import oracle  # test infrastructure: used only for this reference timing
+    from threadpoolctl import threadpool_limits
+    cfg = dec["cfg"]
+    cache = dec["cache"][0].cpu().numpy()
+    cb = dec["cb"].cpu().numpy()
+    q = dec["qs"][0].float().cpu().numpy()
+    lens = dec["lens"]
+    model, nproc = _cpu_info()
+    done_tokens = 0
+    done_req = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(len(lens)):
+            oracle.decode_attention(q[b], cache, dec["bt_np"][b], int(lens[b]), cb[0], 1, cfg.Tc, cfg.c,
+                                    cfg.bits, cfg.base)
+            done_tokens += int(lens[b])
+            done_req += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    el = time.perf_counter() - t0
+    return {"value": done_tokens / el, "unit": "cached tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_req} of {len(lens)} requests of the same 32K-context batch (all 16 KV heads, "
+                      f"loop step 1), fp64 NumPy with BLAS limited to 1 thread, {el:.1f} s",
+            "cpu_model": model, "host_cpus": nproc}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-encode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB copy kernel (reference for PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path is not sharded "
+              "across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import decode_attention_loopvq_amd as lv
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    lv.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    dec = bench_decode(args, torch, np, synth, lv)
+    enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
+    cfg = dec["cfg"]
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 1),
+        "unit": "cached tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (loop-correlated Gaussian K/V encoded on the GPU; fp16 codebooks from a "
+                "synthetic calibration set; bf16 queries)",
+        "config": {"workload": f"{cfg.name}: decode attention, B={len(dec['lens'])}, N={dec['max_seq_len']}, "
+                               f"H_kv=H_q={cfg.H_kv}, D={cfg.D}, c={cfg.c}, Tc={cfg.Tc}, K={cfg.K} (8-bit), "
+                               f"P={cfg.page_size}, one loop step per call, t cycling 1..4",
+                   "global_batch": len(dec["lens"]), "seq_len": dec["max_seq_len"], "parallelism": "none (1 GPU)"},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode_split_ms": round(dec["split_avg_ms"], 5),
+        "decode_combine_ms": round(dec["combine_avg_ms"], 5),
+        "per_loop_step_tokens_per_s": {k: round(v, 1) for k, v in dec["per_t_tokens_per_s"].items()},
+        "encode": enc,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+"""ctypes binding of libloopvq.so (argument marshalling only).
+
+Every function keeps the C name.  Tensors must already live where the C ABI
+expects them (device tensors on the current HIP device, except the host RoPE
+table), with the documented dtype and a contiguous layout.  Work is enqueued
+on torch's current stream.  A nonzero status raises LoopVQError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libloopvq.so")
+
+LOOPVQ_DTYPE_F32 = 0
+LOOPVQ_DTYPE_BF16 = 1
+
+
+class LoopVQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({loopvq_status_string(status)})")
+        self.status = status
+
+
+class loopvq_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("D", "c", "Tc", "T", "bits", "K", "H_kv", "H_q", "page_size", "x_dtype", "io_dtype")]
+
+    @classmethod
+    def make(cls, D, c, Tc, T, bits, H_kv, H_q, page_size, x_dtype="bf16", io_dtype="bf16"):
+        dt = {"f32": LOOPVQ_DTYPE_F32, "bf16": LOOPVQ_DTYPE_BF16}
+        return cls(D, c, Tc, T, bits, 1 << bits, H_kv, H_q, page_size,
+                   dt.get(x_dtype, x_dtype), dt.get(io_dtype, io_dtype))
+
+    @property
+    def G(self):
+        return self.c * self.Tc
+
+    @property
+    def n_blocks(self):
+        return self.T // self.Tc
+
+    @property
+    def row_bytes(self):
+        return self.D // self.c * self.bits // 8
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m decode_attention_loopvq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int32
+        D = ctypes.POINTER(loopvq_dims)
+        L.loopvq_status_string.restype = ctypes.c_char_p
+        L.loopvq_status_string.argtypes = [ctypes.c_int]
+        L.loopvq_row_bytes.restype = ctypes.c_int
+        L.loopvq_row_bytes.argtypes = [D]
+        L.loopvq_build_codebook_slices.restype = ctypes.c_int
+        L.loopvq_build_codebook_slices.argtypes = [D, P, P, P, P]
+        L.loopvq_rope_table.restype = ctypes.c_int
+        L.loopvq_rope_table.argtypes = [I, I, ctypes.c_double, P]
+        L.loopvq_encode.restype = ctypes.c_int
+        L.loopvq_encode.argtypes = [D, I, I, I, P, P, P, P, P, P, ctypes.c_int64, P]
+        L.loopvq_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.loopvq_decode_workspace_bytes.argtypes = [D, I, I]
+        L.loopvq_decode_attn.restype = ctypes.c_int
+        L.loopvq_decode_attn.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.c_float,
+                                         P, P, P, ctypes.c_size_t, P]
+        L.loopvq_decode_split.restype = ctypes.c_int
+        L.loopvq_decode_split.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.c_float, P,
+                                          ctypes.c_size_t, P]
+        L.loopvq_decode_combine.restype = ctypes.c_int
+        L.loopvq_decode_combine.argtypes = [D, I, P, I, P, P, P, ctypes.c_size_t, P]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_slices",
+            "loopvq_rope_table", "loopvq_encode", "loopvq_decode_workspace_bytes",
+            "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise LoopVQError(status, what)
+
+
+def _need(t: torch.Tensor, dtype, name: str, device: bool = True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def loopvq_status_string(status: int) -> str:
+    return lib().loopvq_status_string(int(status)).decode()
+
+
+def loopvq_row_bytes(dims: loopvq_dims) -> int:
+    r = lib().loopvq_row_bytes(ctypes.byref(dims))
+    if r < 0:
+        raise LoopVQError(r, "loopvq_row_bytes")
+    return r
+
+
+def loopvq_build_codebook_slices(dims: loopvq_dims, cb: torch.Tensor, slices=None, hsq=None):
+    """cb [n_blocks][H_kv][2][K][G] fp16 -> (slices [T][H_kv][2][K][c] fp16, hsq fp32)."""
+    _need(cb, torch.float16, "cb")
+    if slices is None:
+        slices = torch.empty((dims.T, dims.H_kv, 2, dims.K, dims.c), dtype=torch.float16, device=cb.device)
+    if hsq is None:
+        hsq = torch.empty((dims.n_blocks, dims.H_kv, 2, dims.K), dtype=torch.float32, device=cb.device)
+    _check(lib().loopvq_build_codebook_slices(ctypes.byref(dims), _ptr(cb), _ptr(slices), _ptr(hsq),
+                                              _stream()), "loopvq_build_codebook_slices")
+    return slices, hsq
+
+
+def loopvq_rope_table(max_pos: int, D: int, base: float = 10000.0) -> torch.Tensor:
+    """Host table [max_pos * D] float32 in the decode kernel's layout."""
+    t = torch.empty(max(max_pos, 0) * D, dtype=torch.float32)
+    _check(lib().loopvq_rope_table(int(max_pos), int(D), float(base), _ptr(t) if max_pos > 0 else None),
+           "loopvq_rope_table")
+    return t
+
+
+def loopvq_encode(dims: loopvq_dims, xk: torch.Tensor, xv: torch.Tensor, cb: torch.Tensor,
+                  hsq: torch.Tensor, slot_mapping: torch.Tensor, index_cache: torch.Tensor,
+                  first_block: int = 0, n_blocks: Optional[int] = None,
+                  block_stride_bytes: Optional[int] = None) -> None:
+    """Encode xk, xv [n_blocks*Tc][n_tok][H_kv][D] into index_cache (uint8).
+
+    cb / hsq hold all blocks of the layer; index_cache holds the cache of
+    `first_block` first, the next block `block_stride_bytes` later.
+    """
+    xdt = torch.float32 if dims.x_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+    _need(xk, xdt, "xk"); _need(xv, xdt, "xv")
+    _need(cb, torch.float16, "cb"); _need(hsq, torch.float32, "hsq")
+    _need(slot_mapping, torch.int32, "slot_mapping"); _need(index_cache, torch.uint8, "index_cache")
+    if n_blocks is None:
+        n_blocks = xk.shape[0] // dims.Tc
+    n_tok = xk.shape[1]
+    if xk.shape != xv.shape or xk.shape[0] != n_blocks * dims.Tc or slot_mapping.numel() != n_tok:
+        raise ValueError("encode: inconsistent shapes")
+    if block_stride_bytes is None:
+        block_stride_bytes = index_cache.numel() // max(n_blocks, 1) if n_blocks > 1 else 0
+    _check(lib().loopvq_encode(ctypes.byref(dims), n_tok, first_block, n_blocks, _ptr(xk), _ptr(xv),
+                               _ptr(cb), _ptr(hsq), _ptr(slot_mapping), _ptr(index_cache),
+                               int(block_stride_bytes), _stream()), "loopvq_encode")
+
+
+def loopvq_decode_workspace_bytes(dims: loopvq_dims, B: int, max_seq_len: int) -> int:
+    return int(lib().loopvq_decode_workspace_bytes(ctypes.byref(dims), int(B), int(max_seq_len)))
+
+
+def loopvq_decode_attn(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: torch.Tensor,
+                       slices: torch.Tensor, rope_table: torch.Tensor, block_table: torch.Tensor,
+                       seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float = 0.0,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, max_pos: Optional[int] = None):
+    """Decode attention at loop step t; returns (out [B][H_q][D], lse [B][H_q] or None)."""
+    iodt = torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+    _need(q, iodt, "q"); _need(index_cache, torch.uint8, "index_cache")
+    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
+    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.H_q, dims.D), dtype=iodt, device=q.device)
+    _need(out, iodt, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if max_pos is None:
+        max_pos = rope_table.numel() // dims.D
+    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+    _check(lib().loopvq_decode_attn(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
+                                    _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
+                                    int(max_pages), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+                                    _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()),
+                                    _stream()), "loopvq_decode_attn")
+    return out, lse
+
+
+def loopvq_decode_split(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: torch.Tensor,
+                        slices: torch.Tensor, rope_table: torch.Tensor, block_table: torch.Tensor,
+                        seq_lens: torch.Tensor, max_seq_len: int, workspace: torch.Tensor,
+                        sm_scale: float = 0.0, max_pos: Optional[int] = None) -> None:
+    """Split-K pass of decode attention; partials are left in `workspace`."""
+    if max_pos is None:
+        max_pos = rope_table.numel() // dims.D
+    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+    _check(lib().loopvq_decode_split(ctypes.byref(dims), int(t), q.shape[0], _ptr(q), _ptr(index_cache),
+                                     _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
+                                     int(max_pages), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+                                     _ptr(workspace), int(workspace.numel()), _stream()), "loopvq_decode_split")
+
+
+def loopvq_decode_combine(dims: loopvq_dims, B: int, seq_lens: torch.Tensor, max_seq_len: int,
+                          workspace: torch.Tensor, out: torch.Tensor,
+                          lse: Optional[torch.Tensor] = None) -> None:
+    """Merge the split partials in `workspace` into out (and lse)."""
+    _check(lib().loopvq_decode_combine(ctypes.byref(dims), int(B), _ptr(seq_lens), int(max_seq_len), _ptr(out),
+                                       _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream()),
+           "loopvq_decode_combine")

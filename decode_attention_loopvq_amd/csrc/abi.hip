@@ -1,0 +1,273 @@
+// C ABI of the LoopVQ library: host-side validation, work planning and launches.
+// Every check runs before anything is enqueued, so a call that fails has
+// launched nothing.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+#include "loopvq.h"
+
+using namespace loopvq;
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) { int r = 0; while ((1 << r) < x) ++r; return r; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_dims(const loopvq_dims* d) {
+  if (d == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  if (d->D <= 0 || d->c <= 0 || d->Tc <= 0 || d->T <= 0 || d->H_kv <= 0 || d->H_q <= 0)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (d->D % d->c != 0 || d->T % d->Tc != 0 || d->H_q % d->H_kv != 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (d->bits <= 0 || d->bits > 16 || d->K != (1 << d->bits)) return LOOPVQ_ERR_INVALID_ARG;
+  if (!is_pow2(d->page_size) || d->page_size < 8 || d->page_size > 1024) return LOOPVQ_ERR_INVALID_ARG;
+  if ((d->x_dtype != LOOPVQ_DTYPE_F32 && d->x_dtype != LOOPVQ_DTYPE_BF16) ||
+      (d->io_dtype != LOOPVQ_DTYPE_F32 && d->io_dtype != LOOPVQ_DTYPE_BF16))
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (d->bits != 4 && d->bits != 8) return LOOPVQ_ERR_UNSUPPORTED;
+  if (d->D != 64 && d->D != 128) return LOOPVQ_ERR_UNSUPPORTED;
+  if (d->c != 2 && d->c != 4 && d->c != 8) return LOOPVQ_ERR_UNSUPPORTED;
+  if ((d->D / d->c) % 8 != 0) return LOOPVQ_ERR_UNSUPPORTED;
+  const int G = d->c * d->Tc;
+  if (G != 8 && G != 16 && G != 32) return LOOPVQ_ERR_UNSUPPORTED;
+  if (G == 8 && d->x_dtype != LOOPVQ_DTYPE_F32) return LOOPVQ_ERR_UNSUPPORTED;
+  return LOOPVQ_OK;
+}
+
+struct DecodePlan {
+  int grp, n_pairs, NP, NT, n_pg, Lc, n_chunks, items_per_head, wg_per_head, grid;
+  size_t n_part, bytes_o, bytes_lse;
+};
+
+// One wave step covers NP (request, query head) pairs x NT = 16 / NP
+// consecutive positions; a wave owns one pair group and one chunk of Lc
+// positions; four waves of a workgroup share a KV head (and its LDS slices).
+DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
+  DecodePlan pl{};
+  pl.grp = d->H_q / d->H_kv;
+  pl.n_pairs = B * pl.grp;
+  pl.NP = 1;
+  while (pl.NP < 4 && pl.NP < pl.n_pairs) pl.NP <<= 1;
+  pl.NT = 16 / pl.NP;
+  pl.n_pg = std::max(1, (pl.n_pairs + pl.NP - 1) / pl.NP);
+  const long long len = std::max(max_seq_len, 1);
+  // about 2048 waves (8 per CU) over the whole call
+  const long long work = (long long)d->H_kv * pl.n_pg * len;
+  const long long step2 = 2LL * pl.NT;
+  long long Lc = (work + 2047) / 2048;
+  Lc = (Lc + step2 - 1) / step2 * step2;
+  Lc = std::max(Lc, step2);
+  Lc = std::min(Lc, (len + step2 - 1) / step2 * step2);
+  pl.Lc = (int)Lc;
+  pl.n_chunks = (int)((len + pl.Lc - 1) / pl.Lc);
+  pl.items_per_head = pl.n_pg * pl.n_chunks;
+  pl.wg_per_head = (pl.items_per_head + 3) / 4;
+  pl.grid = d->H_kv * pl.wg_per_head;
+  pl.n_part = (size_t)d->H_kv * std::max(pl.n_pairs, 1) * pl.n_chunks;
+  pl.bytes_o = align256(pl.n_part * d->D * sizeof(float));
+  pl.bytes_lse = align256(pl.n_part * sizeof(float));
+  return pl;
+}
+
+bool decode_supported(int D, int c, int bits) {
+  if (D == 128) return c == 2 || c == 4 || c == 8;
+  return (c == 2 || c == 4) || (c == 8 && bits == 8);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LOOPVQ_OK : LOOPVQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* loopvq_status_string(int status) {
+  switch (status) {
+    case LOOPVQ_OK: return "ok";
+    case LOOPVQ_ERR_INVALID_ARG: return "invalid argument";
+    case LOOPVQ_ERR_UNSUPPORTED: return "unsupported shape, code width or dtype";
+    case LOOPVQ_ERR_WORKSPACE: return "workspace too small";
+    case LOOPVQ_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int loopvq_row_bytes(const loopvq_dims* dims) {
+  const int st = check_dims(dims);
+  if (st != LOOPVQ_OK) return st;
+  return dims->D / dims->c * dims->bits / 8;
+}
+
+int loopvq_build_codebook_slices(const loopvq_dims* dims, const void* cb, void* slices, float* hsq,
+                                 hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != LOOPVQ_OK) return st;
+  if (cb == nullptr || slices == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  return hip_status(launch_build_slices((const uint16_t*)cb, (uint16_t*)slices, hsq, dims->T / dims->Tc,
+                                        dims->H_kv, dims->K, dims->c, dims->Tc, stream));
+}
+
+int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table) {
+  if (max_pos < 0 || (D != 64 && D != 128) || !(base > 1.0)) return LOOPVQ_ERR_INVALID_ARG;
+  if (max_pos > 0 && table == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  const int nch = D / 16;
+  for (int64_t p = 0; p < max_pos; ++p) {
+    for (int j = 0; j < nch; ++j) {
+      for (int i = 0; i < 4; ++i) {
+        float* o = table + (((size_t)p * nch + j) * 4 + i) * 4;
+        for (int e = 0; e < 2; ++e) {
+          const int f = i * (D / 8) + 2 * j + e;
+          const double theta = pow(base, -2.0 * f / D);
+          const double ang = (double)p * theta;
+          o[2 * e] = (float)cos(ang);
+          o[2 * e + 1] = (float)sin(ang);
+        }
+      }
+    }
+  }
+  return LOOPVQ_OK;
+}
+
+int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
+                  const void* xk, const void* xv, const void* cb, const float* hsq,
+                  const int32_t* slot_mapping, uint8_t* index_cache, int64_t block_stride_bytes,
+                  hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != LOOPVQ_OK) return st;
+  const int nb_total = dims->T / dims->Tc;
+  if (n_tok < 0 || first_block < 0 || n_blocks < 1 || first_block + n_blocks > nb_total)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (n_blocks > 1 && block_stride_bytes <= 0) return LOOPVQ_ERR_INVALID_ARG;
+  if ((dims->D / dims->c) % 16 != 0) return LOOPVQ_ERR_UNSUPPORTED;
+  if (n_tok == 0) return LOOPVQ_OK;
+  if (!xk || !xv || !cb || !hsq || !slot_mapping || !index_cache) return LOOPVQ_ERR_INVALID_ARG;
+  const int H = dims->H_kv, K = dims->K, G = dims->c * dims->Tc;
+  EncodeParams p{};
+  p.xk = xk;
+  p.xv = xv;
+  p.cb = (const uint16_t*)cb + (size_t)first_block * H * 2 * K * G;
+  p.hsq = hsq + (size_t)first_block * H * 2 * K;
+  p.slot_mapping = slot_mapping;
+  p.cache = index_cache;
+  p.block_stride = block_stride_bytes;
+  p.n_tok = n_tok;
+  p.H_kv = H;
+  p.D = dims->D;
+  p.c = dims->c;
+  p.Tc = dims->Tc;
+  p.K = K;
+  p.log2P = ilog2(dims->page_size);
+  const long long streams = (long long)n_blocks * 2 * H;
+  long long tpw = (streams * n_tok + 4LL * 2048 - 1) / (4LL * 2048);
+  tpw = std::max<long long>(1, std::min<long long>(tpw, n_tok));
+  p.tok_per_wave = (int)tpw;
+  p.n_tok_groups = (int)((n_tok + 4 * tpw - 1) / (4 * tpw));
+  return hip_status(launch_encode(G, dims->x_dtype == LOOPVQ_DTYPE_F32, dims->bits, p, n_blocks, stream));
+}
+
+size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {
+  if (check_dims(dims) != LOOPVQ_OK || B < 0 || max_seq_len < 0) return 0;
+  const DecodePlan pl = plan_decode(dims, B, max_seq_len);
+  return pl.bytes_o + pl.bytes_lse;
+}
+
+static int check_decode_common(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {
+  int st = check_dims(dims);
+  if (st != LOOPVQ_OK) return st;
+  if (B < 0 || max_seq_len < 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (!decode_supported(dims->D, dims->c, dims->bits)) return LOOPVQ_ERR_UNSUPPORTED;
+  return LOOPVQ_OK;
+}
+
+int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                        const uint8_t* index_cache, const void* slices, const float* rope_table,
+                        int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int st = check_decode_common(dims, B, max_seq_len);
+  if (st != LOOPVQ_OK) return st;
+  if (t < 1 || t > dims->T || max_pos < 0 || max_pages < 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (max_seq_len > max_pos || (long long)max_seq_len > (long long)max_pages * dims->page_size)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (B == 0) return LOOPVQ_OK;
+  if (!q || !index_cache || !slices || !rope_table || !block_table || !seq_lens || !workspace)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  const DecodePlan pl = plan_decode(dims, B, max_seq_len);
+  if (workspace_bytes < pl.bytes_o + pl.bytes_lse) return LOOPVQ_ERR_WORKSPACE;
+
+  DecodeParams p{};
+  p.q = q;
+  p.cache = index_cache;
+  p.slices = (const uint16_t*)slices + (size_t)(t - 1) * dims->H_kv * 2 * dims->K * dims->c;
+  p.rope = rope_table;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + pl.bytes_o);
+  p.B = B;
+  p.H_kv = dims->H_kv;
+  p.H_q = dims->H_q;
+  p.grp = pl.grp;
+  p.max_pages = max_pages;
+  p.log2P = ilog2(dims->page_size);
+  p.n_pairs = pl.n_pairs;
+  p.NP = pl.NP;
+  p.NT = pl.NT;
+  p.n_pg = pl.n_pg;
+  p.Lc = pl.Lc;
+  p.n_chunks = pl.n_chunks;
+  p.items_per_head = pl.items_per_head;
+  p.wg_per_head = pl.wg_per_head;
+  p.max_seq_len = max_seq_len;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)dims->D);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(launch_decode_split(dims->D, dims->c, dims->bits, dims->io_dtype == LOOPVQ_DTYPE_F32, p,
+                                        pl.grid, stream));
+}
+
+int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq_lens, int32_t max_seq_len,
+                          void* out, float* lse, const void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int st = check_decode_common(dims, B, max_seq_len);
+  if (st != LOOPVQ_OK) return st;
+  if (B == 0) return LOOPVQ_OK;
+  if (!seq_lens || !out || !workspace) return LOOPVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  const DecodePlan pl = plan_decode(dims, B, max_seq_len);
+  if (workspace_bytes < pl.bytes_o + pl.bytes_lse) return LOOPVQ_ERR_WORKSPACE;
+  CombineParams cp{};
+  cp.part_o = (const float*)workspace;
+  cp.part_lse = (const float*)((const char*)workspace + pl.bytes_o);
+  cp.seq_lens = seq_lens;
+  cp.out = out;
+  cp.lse = lse;
+  cp.B = B;
+  cp.H_q = dims->H_q;
+  cp.grp = pl.grp;
+  cp.n_pairs = pl.n_pairs;
+  cp.n_chunks = pl.n_chunks;
+  cp.Lc = pl.Lc;
+  cp.max_seq_len = max_seq_len;
+  return hip_status(launch_decode_combine(dims->D, dims->io_dtype == LOOPVQ_DTYPE_BF16, cp, stream));
+}
+
+int loopvq_decode_attn(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                       const uint8_t* index_cache, const void* slices, const float* rope_table,
+                       int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                       const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_decode_common(dims, B, max_seq_len);
+  if (st != LOOPVQ_OK) return st;
+  if (B > 0 && out == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  st = loopvq_decode_split(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages,
+                           seq_lens, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+  if (st != LOOPVQ_OK) return st;
+  return loopvq_decode_combine(dims, B, seq_lens, max_seq_len, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Kernel parameter blocks and launchers shared between the C ABI layer and
+// the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace loopvq {
+
+struct DecodeParams {
+  const void* q;              // [B][H_q][D] bf16 or fp32
+  const uint8_t* cache;       // [num_pages][H_kv][2][P][R]
+  const void* slices;         // slice of the step: [H_kv][2][K][C] fp16
+  const float* rope;          // [max_pos][D/16][4][4]
+  const int32_t* block_table; // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  float* part_o;              // [H_kv][n_pairs][n_chunks][D]
+  float* part_lse;            // [H_kv][n_pairs][n_chunks], log2 domain
+  int B, H_kv, H_q, grp, max_pages, log2P;
+  int n_pairs;                // B * grp (request, query head) pairs per KV head
+  int NP, NT;                 // pairs per wave (1, 2 or 4) and positions per wave step (16 / NP)
+  int n_pg;                   // pair groups per KV head
+  int Lc;                     // positions per chunk (one wave), a multiple of 2 * NT
+  int n_chunks;
+  int items_per_head;         // n_pg * n_chunks wave work items per KV head
+  int wg_per_head;            // ceil(items_per_head / 4)
+  int max_seq_len;            // host bound; seq_lens are clamped to it
+  float scale_log2;           // sm_scale * log2(e)
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int B, H_q, grp, n_pairs, n_chunks, Lc, max_seq_len;
+};
+
+struct EncodeParams {
+  const void* xk;             // [n_blocks*Tc][n_tok][H_kv][D]
+  const void* xv;
+  const uint16_t* cb;         // [n_blocks][H_kv][2][K][G] fp16 of the first block
+  const float* hsq;           // [n_blocks][H_kv][2][K]
+  const int32_t* slot_mapping;
+  uint8_t* cache;             // cache of the first block
+  int64_t block_stride;
+  int n_tok, H_kv, D, c, Tc, K, log2P;
+  int tok_per_wave;
+  int n_tok_groups;           // ceil(n_tok / (4 * tok_per_wave))
+};
+
+hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
+                               hipStream_t s);
+hipError_t launch_decode_combine(int D, bool out_bf16, const CombineParams& p, hipStream_t s);
+hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_build_slices(const uint16_t* cb, uint16_t* slices, float* hsq, int n_blocks, int H_kv,
+                               int K, int c, int Tc, hipStream_t s);
+
+}  // namespace loopvq

@@ -1,0 +1,214 @@
+/*
+ * loopvq.h - C ABI of the LoopVQ encoder and quantised decode-attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * LoopVQ ("LoopVQ: Sub 1-bit KV Cache Quantization for Looped Transformers",
+ * hub.valency.io/works/W_7srt5hed_v1) quantises the KV cache of a looped
+ * transformer along the loop axis: T loop steps are cut into blocks of Tc
+ * consecutive steps, and one b-bit code covers c channels at each of the Tc
+ * steps of a block (a coupled vector of G = c*Tc elements, section 4.1,
+ * eq. 4).  Loop step beta*Tc + m + 1 reads the shared code through its own
+ * slice of the codebook entry, coordinates i*Tc + m for i < c (eq. 5 and
+ * section 4 "System implementation").  Keys are coded before RoPE, and the
+ * decode kernel applies RoPE to every rebuilt key (section 2, App. C).
+ *
+ * Conventions
+ *   - Every pointer is a device pointer unless marked [host].  The caller owns
+ *     every buffer; the library allocates and frees no memory and keeps no
+ *     state between calls, so calls on different streams are independent.
+ *   - All device work is enqueued on the given stream; no call synchronises.
+ *   - Every argument is validated on the host before anything is launched;
+ *     a call that returns an error has enqueued nothing.
+ *   - Functions return LOOPVQ_OK (0) or a negative status; no C++ exception
+ *     crosses this interface.
+ *   - Device faults (for example a block-table entry outside the index cache)
+ *     are undefined behaviour and surface as HIP errors on the caller's next
+ *     synchronisation.
+ *
+ * Data layouts
+ *   codebook  cb     [n_blocks][H_kv][2][K][G] fp16, entry coordinate
+ *                    u = i*Tc + m (channel-major, loop-minor), index 1 = K|V.
+ *   slices           [T][H_kv][2][K][c] fp16: slice of loop step t (0-based
+ *                    here) holds coordinates i*Tc + (t mod Tc) of each entry.
+ *   hsq              [n_blocks][H_kv][2][K] fp32: 0.5*||e||^2 of each entry.
+ *   index cache      one cache per block beta: [num_pages][H_kv][2][P][R]
+ *                    bytes, R = (D/c)*bits/8 bytes per row.  Page p holds the
+ *                    rows of tokens p*P .. p*P+P-1 of whichever request maps
+ *                    a logical page to it through its block table.
+ *   row order        A row stores the n = D/c codes of one token in the
+ *                    "RoPE-pair interleaved" slot order: with h = n/2 and
+ *                    q = n/8, slot s = i*2q + r (i < 4, r < 2q) holds group
+ *                    g(s) = i*q + r when r < q and h + i*q + (r - q) otherwise,
+ *                    so the groups {g, g + h} whose channels RoPE rotates
+ *                    together sit side by side.  8-bit: slot s is byte s.
+ *                    4-bit: slot s is the low nibble of byte s/2 when s is
+ *                    even, the high nibble when odd.
+ *   rope table       [max_pos][D/16][4][4] fp32 (see loopvq_rope_table).
+ *   q, out           [B][H_q][D], query head j reads KV head j / (H_q/H_kv).
+ */
+#ifndef LOOPVQ_H
+#define LOOPVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LOOPVQ_OK = 0,
+  LOOPVQ_ERR_INVALID_ARG = -1,      /* null pointer, inconsistent sizes, bad t, ...     */
+  LOOPVQ_ERR_UNSUPPORTED = -2,      /* valid but not compiled: bits, c, D, dtype, ...   */
+  LOOPVQ_ERR_WORKSPACE = -3,        /* decode workspace smaller than required           */
+  LOOPVQ_ERR_HIP = -4               /* a HIP launch or runtime call failed              */
+};
+
+enum { LOOPVQ_DTYPE_F32 = 0, LOOPVQ_DTYPE_BF16 = 1 };
+
+typedef struct loopvq_dims {
+  int32_t D;          /* head dimension: 64 or 128                                      */
+  int32_t c;          /* channels per loop step covered by one code: 2, 4 or 8          */
+  int32_t Tc;         /* loop steps per block (one code serves Tc steps); Tc | T        */
+  int32_t T;          /* loop steps                                                     */
+  int32_t bits;       /* code width: 4 or 8                                             */
+  int32_t K;          /* codebook entries, must equal 1 << bits                         */
+  int32_t H_kv;       /* KV heads                                                       */
+  int32_t H_q;        /* query heads, a multiple of H_kv                                */
+  int32_t page_size;  /* tokens per page P: a power of two in [16, 256]                 */
+  int32_t x_dtype;    /* encoder input K/V: LOOPVQ_DTYPE_F32 or LOOPVQ_DTYPE_BF16        */
+  int32_t io_dtype;   /* decode query and output: LOOPVQ_DTYPE_F32 or LOOPVQ_DTYPE_BF16  */
+} loopvq_dims;
+/* Supported shapes: D in {64, 128}; D/c a multiple of 8; G = c*Tc in {8, 16, 32}
+ * (G = 8 only with fp32 encoder input); 4-bit codes only with K = 16 and
+ * 8-bit only with K = 256. */
+
+/* Human-readable text of a status code.  Never NULL. */
+const char* loopvq_status_string(int status);
+
+/* Bytes of one index row, (D/c)*bits/8, or a negative status. */
+int loopvq_row_bytes(const loopvq_dims* dims);
+
+/*
+ * Cut the per-loop-step codebook slices once at load time, and compute
+ * hsq = 0.5*||e||^2 of every entry (in fp64, rounded to fp32) for the encoder.
+ * [LoopVQ paper, section 4 "System implementation": the slice B_t holds
+ * coordinate i*Tc + m of every entry, cut once when the model is loaded.]
+ *   n_blocks = T / Tc codebooks per (KV head, K|V).
+ *   cb      [n_blocks][H_kv][2][K][G] fp16 (input)
+ *   slices  [T][H_kv][2][K][c] fp16      (output)
+ *   hsq     [n_blocks][H_kv][2][K] fp32  (output, may be NULL)
+ */
+int loopvq_build_codebook_slices(const loopvq_dims* dims, const void* cb,
+                                 void* slices, float* hsq, hipStream_t stream);
+
+/*
+ * Host-side RoPE coefficient table in the layout the decode kernel streams:
+ * for position p (0 <= p < max_pos), chunk j < D/16 and lane quarter i < 4,
+ * the four floats at ((p*(D/16) + j)*4 + i)*4 are
+ *     cos(p*theta_f), sin(p*theta_f), cos(p*theta_{f+1}), sin(p*theta_{f+1})
+ * with f = i*(D/8) + 2*j and theta_f = base^(-2f/D), computed in fp64 and
+ * rounded to fp32.  [LoopVQ paper, App. C: the kernel reads cos/sin from a
+ * table precomputed for all positions instead of evaluating transcendentals.]
+ *   table [host] must hold max_pos*D*4 bytes.  The caller copies it to the
+ *   device once.
+ */
+int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table);
+
+/*
+ * Encode blocks of pre-RoPE keys and values into the paged index caches.
+ * For every token j, KV head h, x in {K, V}, block beta and group g < D/c,
+ * the coupled vector z[i*Tc + m] = x^(beta*Tc+m+1)[j][h][g*c + i] (eq. 4)
+ * is replaced by the index of its nearest codebook entry in squared L2
+ * distance, ties to the lowest index (eq. 2), and written to slot g's place
+ * in the row of token j.  [LoopVQ paper, section 4 "System implementation",
+ * encoding: distances to all entries as a matrix product, then the nearest
+ * entry.]
+ *   n_tok         tokens in this call (n_tok >= 0; 0 is a no-op).
+ *   n_blocks      blocks encoded, 1 <= n_blocks <= T/Tc; block beta of x is
+ *                 loop steps beta*Tc .. beta*Tc+Tc-1 of the input.
+ *   xk, xv        [n_blocks*Tc][n_tok][H_kv][D], dtype dims->x_dtype.
+ *   cb, hsq       codebooks and 0.5*||e||^2 of blocks first_block ..
+ *                 first_block+n_blocks-1, layouts as above (hsq from
+ *                 loopvq_build_codebook_slices).
+ *   slot_mapping  [n_tok] int32 physical slot page*P + offset of each token.
+ *   index_cache   cache of block first_block; block beta's cache starts at
+ *                 index_cache + (beta - first_block)*block_stride_bytes.
+ * Distances are evaluated as ||z||^2 - 2 z.e + ||e||^2 with fp16 inputs and
+ * fp32 accumulation (bf16 inputs convert exactly to fp16 inside fp16's normal
+ * range; fp32 inputs are split into two fp16 terms), so the index can differ
+ * from an exact evaluation only where two distances lie within fp32 rounding
+ * of each other.
+ */
+int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
+                  int32_t n_blocks, const void* xk, const void* xv,
+                  const void* cb, const float* hsq, const int32_t* slot_mapping,
+                  uint8_t* index_cache, int64_t block_stride_bytes,
+                  hipStream_t stream);
+
+/* Workspace bytes that loopvq_decode_attn needs for this batch shape. */
+size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
+                                     int32_t max_seq_len);
+
+/*
+ * Quantised decode attention of B requests at loop step t (1-based).
+ * [LoopVQ paper, section 4 "System implementation", attention: at loop step
+ * t the kernel looks up each index in B_t, rebuilds K, applies RoPE, and
+ * splits the tokens across workgroups whose partial outputs are merged by
+ * their logsumexp, which recovers the exact softmax; App. C.]
+ *   t             loop step, 1 <= t <= T; reads block (t-1)/Tc, slice t-1.
+ *   q             [B][H_q][D] queries already rotated at their own position.
+ *   index_cache   the cache of block (t-1)/Tc.
+ *   slices        [T][H_kv][2][K][c] fp16 from loopvq_build_codebook_slices.
+ *   rope_table    device copy of loopvq_rope_table(max_pos, D, base).
+ *   block_table   [B][max_pages] int32 physical page of each logical page.
+ *   seq_lens      [B] int32 cached tokens per request, 0 <= seq_lens[b] <=
+ *                 max_seq_len, and max_seq_len <= max_pos, and
+ *                 max_seq_len <= max_pages*P.  Token j of a request sits at
+ *                 RoPE position j.
+ *   sm_scale      softmax scale; <= 0 selects 1/sqrt(D).
+ *   out           [B][H_q][D] attention output (dims->io_dtype).  A request
+ *                 with no cached tokens gets zeros.
+ *   lse           [B][H_q] fp32 natural-log sum of exp(scores), or NULL;
+ *                 -inf for a request with no tokens.
+ *   workspace     at least loopvq_decode_workspace_bytes(dims, B, max_seq_len)
+ *                 bytes of device memory, 256-byte aligned; contents on entry
+ *                 are ignored.
+ */
+int loopvq_decode_attn(const loopvq_dims* dims, int32_t t, int32_t B,
+                       const void* q, const uint8_t* index_cache,
+                       const void* slices, const float* rope_table,
+                       int32_t max_pos, const int32_t* block_table,
+                       int32_t max_pages, const int32_t* seq_lens,
+                       int32_t max_seq_len, float sm_scale, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * The two phases of loopvq_decode_attn as separate calls, for callers that
+ * time or schedule them apart.  loopvq_decode_split runs the split-K pass and
+ * leaves per-split partial outputs and log-sum-exps in the workspace;
+ * loopvq_decode_combine merges them into out and lse.  Both must be given the
+ * same dims, B, seq_lens, max_seq_len and workspace, on the same stream (or
+ * with the caller ordering them).  Arguments mean what they mean for
+ * loopvq_decode_attn.  [LoopVQ paper, section 4 "System implementation":
+ * split partial outputs combined through the logsumexp of their scores.]
+ */
+int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                        const uint8_t* index_cache, const void* slices,
+                        const float* rope_table, int32_t max_pos,
+                        const int32_t* block_table, int32_t max_pages,
+                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq_lens,
+                          int32_t max_seq_len, void* out, float* lse,
+                          const void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPVQ_H */

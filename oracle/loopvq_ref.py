@@ -165,10 +165,41 @@ def encode_stream(x: np.ndarray, E: np.ndarray, Tc: int, c: int, beta: int,
 # index rows  [P1 section 4 "System implementation", cache layout: a quantised
 #              page stores one index row per block; b bits per code]
 # --------------------------------------------------------------------------
-def pack_rows(idx: np.ndarray, bits: int) -> np.ndarray:
-    """Pack codes [N, n_groups] into bytes [N, n_groups*bits/8].
+def row_group_order(n_groups: int) -> np.ndarray:
+    """Group held by each slot of an index row.
 
-    8-bit: one byte per group.  4-bit: two groups per byte, the even group in
+    The row stores the codes in "RoPE-pair interleaved" order: with h = n/2
+    and q = n/8, slot block i (i < 4) holds the q groups i*q .. i*q+q-1
+    followed by their RoPE partners h + i*q .. h + i*q+q-1 (RoPE rotates
+    channel f together with channel f + D/2, i.e. group g with group g + h).
+    The pages fix no byte order inside a row; this is the library's layout.
+    """
+    assert n_groups % 8 == 0
+    h, q = n_groups // 2, n_groups // 8
+    order = []
+    for i in range(4):
+        order += list(range(i * q, i * q + q))
+        order += list(range(h + i * q, h + i * q + q))
+    return np.array(order, dtype=np.int64)
+
+
+def groups_to_slots(idx: np.ndarray) -> np.ndarray:
+    """Codes [N, n_groups] in group order -> the same codes in row slot order."""
+    idx = np.asarray(idx)
+    return idx[:, row_group_order(idx.shape[1])]
+
+
+def slots_to_groups(slots: np.ndarray) -> np.ndarray:
+    slots = np.asarray(slots)
+    out = np.empty_like(slots)
+    out[:, row_group_order(slots.shape[1])] = slots
+    return out
+
+
+def pack_rows(idx: np.ndarray, bits: int) -> np.ndarray:
+    """Pack codes [N, n_slots] (already in slot order) into bytes [N, n_slots*bits/8].
+
+    8-bit: one byte per slot.  4-bit: two slots per byte, the even slot in
     the low nibble.
     """
     idx = np.asarray(idx, dtype=np.int64)
@@ -262,8 +293,14 @@ def rope_table(max_pos: int, D: int, base: float) -> np.ndarray:
 #   tokens - so the reference is plain dense softmax attention]
 # --------------------------------------------------------------------------
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
-    """o = softmax(sm_scale * k @ q) @ v and lse = log sum exp(sm_scale * k @ q)."""
+    """o = softmax(sm_scale * k @ q) @ v and lse = log sum exp(sm_scale * k @ q).
+
+    With no keys the softmax is empty; the output is then taken to be zero and
+    the lse -inf (the sum of no exponentials is 0).
+    """
     q = np.asarray(q, dtype=np.float64)
+    if np.asarray(k).shape[0] == 0:
+        return np.zeros(np.asarray(v).shape[1]), -np.inf
     s = sm_scale * (np.asarray(k, dtype=np.float64) @ q)
     mx = s.max()
     w = np.exp(s - mx)
@@ -294,8 +331,8 @@ def decode_attention(q: np.ndarray, cache_block: np.ndarray, block_table_row: np
     o = np.zeros((H_q, D))
     lse = np.zeros(H_q)
     for h in range(H_kv):
-        ki = unpack_rows(gather_rows(cache_block, block_table_row, n, h, 0), bits, ng)
-        vi = unpack_rows(gather_rows(cache_block, block_table_row, n, h, 1), bits, ng)
+        ki = slots_to_groups(unpack_rows(gather_rows(cache_block, block_table_row, n, h, 0), bits, ng))
+        vi = slots_to_groups(unpack_rows(gather_rows(cache_block, block_table_row, n, h, 1), bits, ng))
         khat = rebuild(ki, cb_block[h, 0], Tc, c, m)
         vhat = rebuild(vi, cb_block[h, 1], Tc, c, m)
         krot = rope(khat, pos, base)
@@ -324,7 +361,7 @@ def build_index_cache(xk: np.ndarray, xv: np.ndarray, cb: np.ndarray, Tc: int, c
                 idx, res = encode_stream(x[:, :, h, :], cb[beta, h, kv], Tc, c, beta, method)
                 results[(beta, h, kv)] = res
                 ties += int(res.near_tie.sum())
-                scatter_rows(caches[beta], pack_rows(idx, bits), slots, h, kv)
+                scatter_rows(caches[beta], pack_rows(groups_to_slots(idx), bits), slots, h, kv)
     return caches, ties, results
 
 

@@ -7,5 +7,5 @@ is shared by the oracle side and the GPU side of every test and by the bench.
 from .workloads import (  # noqa: F401
     CONFIGS, Config, config_by_name, round_to_bf16, round_to_f16,
     loop_correlated, channel_scales, make_kv, make_codebooks, make_queries,
-    make_seq_lens, make_block_table, slot_mapping_for, random_index_cache,
+    make_seq_lens, make_block_table, slot_mapping_for, random_index_cache, make_kv_torch,
 )

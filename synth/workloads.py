@@ -273,3 +273,30 @@ def random_index_cache(cfg: Config, num_pages: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return rng.integers(0, 256, size=(num_pages, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes),
                         dtype=np.uint8)
+
+
+def make_kv_torch(cfg: Config, n_tok: int, seed: int, device="cuda", dtype=None):
+    """The same loop-axis recurrence drawn with torch's generator on `device`.
+
+    For workloads too large to draw on the host (the bench's 32K-context
+    batch).  Uses torch's Philox stream, so values differ from `make_kv` for
+    the same seed; the statistics (rho_t, channel scales, storage rounding)
+    are the same.  Returns (xk, xv), each [T, n_tok, H_kv, D].
+    """
+    import torch
+    dtype = dtype or (torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    sc = torch.from_numpy(channel_scales(cfg)).to(device)
+    out = []
+    for kv in range(2):
+        x = torch.empty((cfg.T, n_tok, cfg.H_kv, cfg.D), dtype=dtype, device=device)
+        prev = torch.randn((n_tok, cfg.H_kv, cfg.D), generator=g, device=device, dtype=torch.float32)
+        x[0] = (prev * sc[kv]).to(dtype)
+        for t in range(1, cfg.T):
+            r = float(cfg.rhos[t - 1])
+            eps = torch.randn((n_tok, cfg.H_kv, cfg.D), generator=g, device=device, dtype=torch.float32)
+            prev = r * prev + (1.0 - r * r) ** 0.5 * eps
+            x[t] = (prev * sc[kv]).to(dtype)
+        out.append(x)
+    return out[0], out[1]

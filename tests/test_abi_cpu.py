@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects every invalid argument before launching anything, and
+its host RoPE table matches the oracle's fp64 cos/sin."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import decode_attention_loopvq_amd as lv
+    if not os.path.exists(lv.LIB_PATH):
+        from decode_attention_loopvq_amd import build
+        build.build(verbose=False)
+    return lv
+
+
+def _dims(lv, **kw):
+    base = dict(D=128, c=4, Tc=4, T=4, bits=8, H_kv=16, H_q=16, page_size=64, x_dtype="bf16", io_dtype="bf16")
+    base.update(kw)
+    return lv.loopvq_dims.make(**base)
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
+
+
+def test_header_symbols_exported(L):
+    hdr = open(os.path.join(ROOT, "include", "loopvq.h")).read()
+    declared = set(re.findall(r"\b(loopvq_[a-z_]+)\s*\(", hdr))
+    assert declared == set(L.EXPORTED)
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.loopvq_status_string(s), str) and L.loopvq_status_string(s)
+
+
+def test_row_bytes(L):
+    assert L.loopvq_row_bytes(_dims(L)) == 32
+    assert L.loopvq_row_bytes(_dims(L, c=8)) == 16
+    assert L.loopvq_row_bytes(_dims(L, D=64, c=2, bits=4, x_dtype="f32")) == 16
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(c=3), -1),                       # D % c
+    (dict(Tc=3), -1),                      # Tc does not divide T
+    (dict(H_q=20), -1),                    # H_q % H_kv
+    (dict(page_size=48), -1),              # not a power of two
+    (dict(page_size=4), -1),
+    (dict(bits=5), -2),                    # K = 32: valid pair, not compiled
+    (dict(D=96), -2),
+    (dict(c=16, Tc=2), -2),
+    (dict(c=2, Tc=4), -2),                 # G = 8 needs fp32 encoder input
+    (dict(x_dtype=7), -1),
+])
+def test_invalid_dims(L, kw, status):
+    assert L.lib().loopvq_row_bytes(ctypes.byref(_dims(L, **kw))) == status
+
+
+def test_bad_K_and_null_dims(L):
+    d = _dims(L)
+    d.K = 128
+    assert L.lib().loopvq_row_bytes(ctypes.byref(d)) == -1
+    assert L.lib().loopvq_row_bytes(None) == -1
+
+
+def test_decode_validation_before_launch(L):
+    lib = L.lib()
+    d = _dims(L)
+    ws = L.loopvq_decode_workspace_bytes(d, 4, 1000)
+    assert ws > 0
+    def call(t=1, B=4, max_pos=1000, max_pages=16, max_seq_len=1000, ws_bytes=ws, ptrs=FAKE, work=FAKE):
+        return lib.loopvq_decode_attn(ctypes.byref(d), t, B, ptrs, ptrs, ptrs, ptrs, max_pos, ptrs, max_pages,
+                                      ptrs, max_seq_len, 0.0, ptrs, None, work, ws_bytes, None)
+    assert call(t=0) == -1
+    assert call(t=5) == -1
+    assert call(B=-1) == -1
+    assert call(max_pos=999) == -1            # positions beyond the RoPE table
+    assert call(max_pages=15) == -1           # block table too short for max_seq_len
+    assert call(ptrs=None) == -1
+    assert call(ws_bytes=ws - 1) == -3
+    assert call(work=ctypes.c_void_p((1 << 20) + 8)) == -1   # workspace not 256-byte aligned
+    assert call(B=0) == 0                     # nothing to do
+    d4 = _dims(L, D=64, c=8, bits=4, Tc=2, T=4)
+    assert lib.loopvq_decode_attn(ctypes.byref(d4), 1, 1, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 1, FAKE, 10, 0.0,
+                                  FAKE, None, FAKE, 1 << 20, None) == -2
+
+
+def test_encode_validation_before_launch(L):
+    lib = L.lib()
+    d = _dims(L)
+    def call(n_tok=10, first=0, nb=1, stride=0, ptr=FAKE):
+        return lib.loopvq_encode(ctypes.byref(d), n_tok, first, nb, ptr, ptr, ptr, ptr, ptr, ptr, stride, None)
+    assert call(n_tok=-1) == -1
+    assert call(first=1) == -1
+    assert call(nb=0) == -1
+    assert call(nb=2) == -1
+    assert call(ptr=None) == -1
+    assert call(n_tok=0, ptr=None) == 0
+    d8 = _dims(L, T=8)
+    assert lib.loopvq_encode(ctypes.byref(d8), 4, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    d_small = _dims(L, D=64, c=8)          # 8 groups per token: encoder needs a multiple of 16
+    assert lib.loopvq_encode(ctypes.byref(d_small), 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+
+
+def test_slices_validation(L):
+    lib = L.lib()
+    assert lib.loopvq_build_codebook_slices(ctypes.byref(_dims(L)), None, FAKE, None, None) == -1
+    assert lib.loopvq_build_codebook_slices(None, FAKE, FAKE, None, None) == -1
+
+
+def test_workspace_bytes_monotone(L):
+    d = _dims(L)
+    a = L.loopvq_decode_workspace_bytes(d, 16, 4096)
+    b = L.loopvq_decode_workspace_bytes(d, 16, 32768)
+    assert 0 < a <= b and a % 256 == 0
+    assert L.loopvq_decode_workspace_bytes(d, -1, 10) == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_table_matches_oracle(L, D):
+    max_pos = 40000
+    t = L.loopvq_rope_table(max_pos, D).numpy().reshape(max_pos, D // 16, 4, 4)
+    cs, sn = oracle.rope_cos_sin(np.arange(max_pos), D, 10000.0)
+    j = np.arange(D // 16)[None, :, None]
+    i = np.arange(4)[None, None, :]
+    for e in range(2):
+        f = (i * (D // 8) + 2 * j + e)[0]
+        for got, want in ((t[:, :, :, 2 * e], cs[:, f]), (t[:, :, :, 2 * e + 1], sn[:, f])):
+            # fp64 values rounded once to fp32: within half an fp32 ulp, plus
+            # 1e-10 for the last-bit difference of theta between libm and NumPy
+            bound = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64) / 2 + 1e-10
+            assert np.all(np.abs(got.astype(np.float64) - want) <= bound)
+
+
+def test_rope_table_validation(L):
+    lib = L.lib()
+    assert lib.loopvq_rope_table(-1, 128, 1e4, FAKE) == -1
+    assert lib.loopvq_rope_table(4, 96, 1e4, FAKE) == -1
+    assert lib.loopvq_rope_table(4, 128, 1e4, None) == -1
+    assert lib.loopvq_rope_table(0, 128, 1e4, None) == 0

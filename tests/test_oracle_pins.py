@@ -251,6 +251,8 @@ def test_attention_matches_library_sdpa_and_logsumexp():
 def test_attention_special_cases():
     rng = np.random.default_rng(8)
     D = 16
+    o, lse = oracle.attention(np.ones(D), np.zeros((0, D)), np.zeros((0, D)), 1.0)
+    assert np.all(o == 0) and lse == -np.inf
     v = rng.standard_normal((1, D))
     o, lse = oracle.attention(rng.standard_normal(D), rng.standard_normal((1, D)), v, 1.0)
     np.testing.assert_array_equal(o, v[0])
@@ -296,7 +298,7 @@ def test_decode_equals_dense_attention_when_codebook_holds_the_data():
 
 def test_gqa_heads_read_their_kv_head():
     rng = np.random.default_rng(10)
-    H_kv, grp, D, c, Tc, bits, N, P = 2, 3, 16, 4, 4, 8, 20, 8
+    H_kv, grp, D, c, Tc, bits, N, P = 2, 3, 32, 4, 4, 8, 20, 8
     cache = rng.integers(0, 256, size=(3, H_kv, 2, P, D // c), dtype=np.uint8)
     bt = np.array([2, 0, 1], dtype=np.int32)
     cbb = rng.standard_normal((H_kv, 2, 256, c * Tc)).astype(np.float16)
@@ -306,3 +308,15 @@ def test_gqa_heads_read_their_kv_head():
     o2, _ = oracle.decode_attention(q[[3, 4, 5, 0, 1, 2]], cache[:, ::-1], bt, N, cbb[::-1], 2,
                                     Tc, c, bits, 1e4)
     np.testing.assert_allclose(o2, o[[3, 4, 5, 0, 1, 2]], rtol=0, atol=1e-13)
+
+
+def test_row_order_hand_worked():
+    g = _golden("row_order.json")
+    for n, order in g["orders"].items():
+        np.testing.assert_array_equal(oracle.row_group_order(int(n)), order)
+    ex = g["example_4bit"]
+    codes = np.array([ex["codes"]])
+    rows = oracle.pack_rows(oracle.groups_to_slots(codes), 4)
+    np.testing.assert_array_equal(rows[0], ex["bytes"])
+    back = oracle.slots_to_groups(oracle.unpack_rows(rows, 4, codes.shape[1]))
+    np.testing.assert_array_equal(back, codes)
