@@ -107,7 +107,8 @@ def bench_decode(args, torch, np, synth, lv):
         t = i % cfg.T + 1
         if ev is not None:
             ev[0].record()
-        lv.loopvq_decode_split(dims, t, qs[t - 1], cache[0], slices, rope, bt, seq, max_seq_len, ws)
+        lv.loopvq_decode_split(dims, t, qs[t - 1], cache[0], slices, rope, bt, seq, max_seq_len, ws,
+                               max_pos=max_seq_len)
         if ev is not None:
             ev[1].record()
         lv.loopvq_decode_combine(dims, B, seq, max_seq_len, ws, out, lse)

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_build_codebook_slices.argtypes = [D, P, P, P, P]
         L.loopvq_rope_table.restype = ctypes.c_int
         L.loopvq_rope_table.argtypes = [I, I, ctypes.c_double, P]
+        L.loopvq_rope_table_floats.restype = ctypes.c_size_t
+        L.loopvq_rope_table_floats.argtypes = [I, I]
         L.loopvq_encode.restype = ctypes.c_int
         L.loopvq_encode.argtypes = [D, I, I, I, P, P, P, P, P, P, ctypes.c_int64, P]
         L.loopvq_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -88,7 +90,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_slices",
-            "loopvq_rope_table", "loopvq_encode", "loopvq_decode_workspace_bytes",
+            "loopvq_rope_table", "loopvq_rope_table_floats", "loopvq_encode", "loopvq_decode_workspace_bytes",
             "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine")
 
 
@@ -138,8 +140,8 @@ def loopvq_build_codebook_slices(dims: loopvq_dims, cb: torch.Tensor, slices=Non
 
 
 def loopvq_rope_table(max_pos: int, D: int, base: float = 10000.0) -> torch.Tensor:
-    """Host table [max_pos * D] float32 in the decode kernel's layout."""
-    t = torch.empty(max(max_pos, 0) * D, dtype=torch.float32)
+    """Host table (float32, loopvq_rope_table_floats(max_pos, D) values) in the decode kernel's layout."""
+    t = torch.empty(int(lib().loopvq_rope_table_floats(int(max_pos), int(D))), dtype=torch.float32)
     _check(lib().loopvq_rope_table(int(max_pos), int(D), float(base), _ptr(t) if max_pos > 0 else None),
            "loopvq_rope_table")
     return t
@@ -194,7 +196,7 @@ def loopvq_decode_attn(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: 
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if max_pos is None:
-        max_pos = rope_table.numel() // dims.D
+        raise ValueError("max_pos (positions covered by rope_table) is required")
     max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
     _check(lib().loopvq_decode_attn(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
                                     _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
@@ -210,7 +212,7 @@ def loopvq_decode_split(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache:
                         sm_scale: float = 0.0, max_pos: Optional[int] = None) -> None:
     """Split-K pass of decode attention; partials are left in `workspace`."""
     if max_pos is None:
-        max_pos = rope_table.numel() // dims.D
+        raise ValueError("max_pos (positions covered by rope_table) is required")
     max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
     _check(lib().loopvq_decode_split(ctypes.byref(dims), int(t), q.shape[0], _ptr(q), _ptr(index_cache),
                                      _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),

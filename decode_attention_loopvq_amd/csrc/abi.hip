@@ -115,10 +115,11 @@ int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table) {
   if (max_pos < 0 || (D != 64 && D != 128) || !(base > 1.0)) return LOOPVQ_ERR_INVALID_ARG;
   if (max_pos > 0 && table == nullptr) return LOOPVQ_ERR_INVALID_ARG;
   const int nch = D / 16;
-  for (int64_t p = 0; p < max_pos; ++p) {
+  const int64_t padded = ((int64_t)max_pos + 3) / 4 * 4;
+  for (int64_t p = 0; p < padded; ++p) {
     for (int j = 0; j < nch; ++j) {
       for (int i = 0; i < 4; ++i) {
-        float* o = table + (((size_t)p * nch + j) * 4 + i) * 4;
+        float* o = table + ((((size_t)(p >> 2) * nch + j) * 4 + i) * 4 + (p & 3)) * 4;
         for (int e = 0; e < 2; ++e) {
           const int f = i * (D / 8) + 2 * j + e;
           const double theta = pow(base, -2.0 * f / D);
@@ -130,6 +131,11 @@ int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table) {
     }
   }
   return LOOPVQ_OK;
+}
+
+size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D) {
+  if (max_pos < 0 || (D != 64 && D != 128)) return 0;
+  return (size_t)(((int64_t)max_pos + 3) / 4 * 4) * D;
 }
 
 int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,

@@ -210,11 +210,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       RowLoad<LB>::load(base + (size_t)(pk & (P - 1)) * R + la * LB, kw);
       RowLoad<LB>::load(base + kv_stride + (size_t)(pv & (P - 1)) * R + lb * LB, vw);
     };
+    // table rows of positions 4g..4g+3 are interleaved: chunk j of quarter la
+    // of position 4g + n sits at float4 ((g*FP + j)*4 + la)*4 + n, so the 16
+    // lanes of a row (4 positions x 4 quarters) read one contiguous 256-B run
     auto table_load = [&](int st, float4v* tb) {
       const int pk = min(gbase + st * NT + lb, last);
-      const float4v* tr = (const float4v*)p.rope + (size_t)pk * FP * 4 + la;
+      const float4v* tr = (const float4v*)p.rope + ((size_t)(pk >> 2) * FP * 4 + la) * 4 + (pk & 3);
 #pragma unroll
-      for (int j = 0; j < FP; ++j) tb[j] = tr[j * 4];
+      for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
     };
 
     // gathered K and V slice entries of the current step

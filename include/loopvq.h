@@ -43,7 +43,7 @@
  *                    together sit side by side.  8-bit: slot s is byte s.
  *                    4-bit: slot s is the low nibble of byte s/2 when s is
  *                    even, the high nibble when odd.
- *   rope table       [max_pos][D/16][4][4] fp32 (see loopvq_rope_table).
+ *   rope table       fp32, positions interleaved in groups of 4 (see loopvq_rope_table).
  *   q, out           [B][H_q][D], query head j reads KV head j / (H_q/H_kv).
  */
 #ifndef LOOPVQ_H
@@ -105,17 +105,21 @@ int loopvq_build_codebook_slices(const loopvq_dims* dims, const void* cb,
                                  void* slices, float* hsq, hipStream_t stream);
 
 /*
- * Host-side RoPE coefficient table in the layout the decode kernel streams:
- * for position p (0 <= p < max_pos), chunk j < D/16 and lane quarter i < 4,
- * the four floats at ((p*(D/16) + j)*4 + i)*4 are
+ * Host-side RoPE coefficient table in the layout the decode kernel streams.
+ * Positions are taken in groups of four (the table is padded to
+ * 4*ceil(max_pos/4) positions); for position p = 4g + n, chunk j < D/16 and
+ * lane quarter i < 4, the four floats at (((g*(D/16) + j)*4 + i)*4 + n)*4 are
  *     cos(p*theta_f), sin(p*theta_f), cos(p*theta_{f+1}), sin(p*theta_{f+1})
  * with f = i*(D/8) + 2*j and theta_f = base^(-2f/D), computed in fp64 and
  * rounded to fp32.  [LoopVQ paper, App. C: the kernel reads cos/sin from a
  * table precomputed for all positions instead of evaluating transcendentals.]
- *   table [host] must hold max_pos*D*4 bytes.  The caller copies it to the
- *   device once.
+ *   table [host] must hold loopvq_rope_table_floats(max_pos, D) floats.  The
+ *   caller copies it to the device once.
  */
 int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table);
+
+/* Floats of the RoPE table for max_pos positions (0 on invalid arguments). */
+size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D);
 
 /*
  * Encode blocks of pre-RoPE keys and values into the paged index caches.

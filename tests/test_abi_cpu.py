@@ -128,11 +128,14 @@ def test_workspace_bytes_monotone(L):
     assert L.loopvq_decode_workspace_bytes(d, -1, 10) == 0
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_rope_table_matches_oracle(L, D):
-    max_pos = 40000
-    t = L.loopvq_rope_table(max_pos, D).numpy().reshape(max_pos, D // 16, 4, 4)
-    cs, sn = oracle.rope_cos_sin(np.arange(max_pos), D, 10000.0)
+@pytest.mark.parametrize("D,max_pos", [(64, 40001), (128, 40000)])
+def test_rope_table_matches_oracle(L, D, max_pos):
+    t = L.loopvq_rope_table(max_pos, D).numpy()
+    padded = (max_pos + 3) // 4 * 4
+    assert t.size == padded * D == L.lib().loopvq_rope_table_floats(max_pos, D)
+    # [position group][chunk j][quarter i][position in group][cos f, sin f, cos f+1, sin f+1]
+    t = t.reshape(padded // 4, D // 16, 4, 4, 4).transpose(0, 3, 1, 2, 4).reshape(padded, D // 16, 4, 4)
+    cs, sn = oracle.rope_cos_sin(np.arange(padded), D, 10000.0)
     j = np.arange(D // 16)[None, :, None]
     i = np.arange(4)[None, None, :]
     for e in range(2):
