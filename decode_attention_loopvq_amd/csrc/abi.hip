@@ -40,24 +40,22 @@ int check_dims(const loopvq_dims* d) {
 }
 
 struct DecodePlan {
-  int grp, n_pairs, NP, NT, n_pg, Lc, n_chunks, items_per_head, wg_per_head, grid;
+  int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid;
   size_t n_part, bytes_o, bytes_lse;
 };
 
-// One wave step covers NP (request, query head) pairs x NT = 16 / NP
-// consecutive positions; a wave owns one pair group and one chunk of Lc
-// positions; four waves of a workgroup share a KV head (and its LDS slices).
+// A wave serves one duo of (request, query head) pairs (2i, 2i+1) over one
+// chunk of Lc positions, NT = 16 consecutive positions per step; the four
+// waves of a workgroup share a KV head (and its LDS slices).
 DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   DecodePlan pl{};
   pl.grp = d->H_q / d->H_kv;
   pl.n_pairs = B * pl.grp;
-  pl.NP = 1;
-  while (pl.NP < 4 && pl.NP < pl.n_pairs) pl.NP <<= 1;
-  pl.NT = 16 / pl.NP;
-  pl.n_pg = std::max(1, (pl.n_pairs + pl.NP - 1) / pl.NP);
+  pl.NT = 16;
+  pl.n_dg = std::max(1, (pl.n_pairs + 1) / 2);
   const long long len = std::max(max_seq_len, 1);
   // about 2048 waves (8 per CU) over the whole call
-  const long long work = (long long)d->H_kv * pl.n_pg * len;
+  const long long work = (long long)d->H_kv * pl.n_dg * len;
   const long long step2 = 2LL * pl.NT;
   long long Lc = (work + 2047) / 2048;
   Lc = (Lc + step2 - 1) / step2 * step2;
@@ -65,7 +63,7 @@ DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   Lc = std::min(Lc, (len + step2 - 1) / step2 * step2);
   pl.Lc = (int)Lc;
   pl.n_chunks = (int)((len + pl.Lc - 1) / pl.Lc);
-  pl.items_per_head = pl.n_pg * pl.n_chunks;
+  pl.items_per_head = pl.n_dg * pl.n_chunks;
   pl.wg_per_head = (pl.items_per_head + 3) / 4;
   pl.grid = d->H_kv * pl.wg_per_head;
   pl.n_part = (size_t)d->H_kv * std::max(pl.n_pairs, 1) * pl.n_chunks;
@@ -115,7 +113,7 @@ int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table) {
   if (max_pos < 0 || (D != 64 && D != 128) || !(base > 1.0)) return LOOPVQ_ERR_INVALID_ARG;
   if (max_pos > 0 && table == nullptr) return LOOPVQ_ERR_INVALID_ARG;
   const int nch = D / 16;
-  const int64_t padded = ((int64_t)max_pos + 3) / 4 * 4;
+  const int64_t padded = ((int64_t)max_pos + 15) / 16 * 16;
   for (int64_t p = 0; p < padded; ++p) {
     for (int j = 0; j < nch; ++j) {
       for (int i = 0; i < 4; ++i) {
@@ -135,7 +133,7 @@ int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table) {
 
 size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D) {
   if (max_pos < 0 || (D != 64 && D != 128)) return 0;
-  return (size_t)(((int64_t)max_pos + 3) / 4 * 4) * D;
+  return (size_t)(((int64_t)max_pos + 15) / 16 * 16) * D;
 }
 
 int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
@@ -222,9 +220,7 @@ int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const voi
   p.max_pages = max_pages;
   p.log2P = ilog2(dims->page_size);
   p.n_pairs = pl.n_pairs;
-  p.NP = pl.NP;
-  p.NT = pl.NT;
-  p.n_pg = pl.n_pg;
+  p.n_dg = pl.n_dg;
   p.Lc = pl.Lc;
   p.n_chunks = pl.n_chunks;
   p.items_per_head = pl.items_per_head;

@@ -81,30 +81,34 @@ __device__ __forceinline__ Entry<EB> lds_entry(const uint8_t* lds, uint32_t addr
   return e;
 }
 
-template <int D, int C, int BITS, bool QF32>
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   constexpr int N = D / C;            // groups per row
   constexpr int Q = N / 8;            // lo (and hi) groups per lane quarter
-  constexpr int F = D / 8;            // RoPE frequencies per lane quarter
-  constexpr int FP = F / 2;           // frequency pairs per quarter (one K MFMA each)
+  constexpr int F = D / 8;            // RoPE frequencies per lane quarter (one K MFMA each)
+  constexpr int FP = F / 2;           // float4 table words per quarter (two frequencies each)
   constexpr int EB = 2 * C;           // bytes of one slice entry
   constexpr int NSLOT = 128 / EB;     // bank windows per 128-byte LDS stripe
   constexpr int R = N * BITS / 8;     // row bytes
   constexpr int LB = R / 4;           // row bytes per lane quarter
   constexpr int LW = (LB + 3) / 4;    // row words per lane
-  constexpr int U = D / 16;           // 4-channel V units per lane
+  constexpr int U = D / 16;           // 4-channel V units per lane and pair
   constexpr int KENT = 1 << BITS;
-  constexpr int SW = 4 * U + 3;       // floats of one lane's softmax state
+  constexpr int NS = SHARE ? 1 : 2;   // index streams per wave: the duo's requests
+  constexpr int NT = 16;              // positions per wave step
+  constexpr int SW = 4 * U + 3;       // floats of one lane's softmax state (one pair)
   constexpr int LDS_SLICES = KENT * 256;
   constexpr int LDS_MERGE = 4 * 64 * SW * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_SLICES > LDS_MERGE ? LDS_SLICES : LDS_MERGE];
 
-  // ---- workgroup -> (KV head, 4 work items); XCD-contiguous order
+  // ---- workgroup -> (KV head, 4 work items).  Heads vary fastest, so each
+  //      XCD (blocks of one residue mod 8, renumbered contiguously) owns a
+  //      band of chunks of every head: its L2 holds only that band's RoPE rows.
   int bid = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int h = bid / p.wg_per_head;
-  const int wgi = bid - h * p.wg_per_head;
+  const int wgi = bid / p.H_kv;
+  const int h = bid - wgi * p.H_kv;
 
   // ---- stage the K and V slices of head h, replicated per bank window
   {
@@ -125,280 +129,341 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- this wave's work item: (pair group, chunk); lane roles
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // ---- this wave's work item (wave-uniform): one duo of pairs, one chunk
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int item = wgi * 4 + wave;
   const bool item_ok = item < p.items_per_head;
-  const int ch = item_ok ? item / p.n_pg : 0;
-  const int pg = item_ok ? item - ch * p.n_pg : 0;
-  const int kslot = lane >> 4;               // pair slot of the 16-lane row
+  const int ch = item_ok ? item / p.n_dg : 0;
+  const int duo = item_ok ? item - ch * p.n_dg : 0;
+  const int row = lane >> 4;                 // position group of this 16-lane row
   const int la = (lane >> 2) & 3, lb = lane & 3;
   // K role: quarter la, position slot lb.  V role: position slot la, quarter lb.
-  const int k = pg * p.NP + kslot % p.NP;
-  const int pgrp = kslot / p.NP;             // position group of this row
-  const bool pair_ok = item_ok && k < p.n_pairs;
-  const int b = pair_ok ? k / p.grp : 0;
-  const int jq = h * p.grp + (pair_ok ? k - (k / p.grp) * p.grp : 0);
-  const int len = pair_ok ? min(max(p.seq_lens[b], 0), p.max_seq_len) : 0;
-  const int p0 = ch * p.Lc;
-  const bool active = item_ok && __ballot(p0 < len) != 0;   // wave-uniform
-
-  float m = -INFINITY, l = 0.f, lx = 0.f;   // running max, sum of rounded p, exact sum of p
-  float4v acc[U];
+  int kq[2], bq[2], len[2];
+  bool okq[2];
 #pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < 2; ++s) {
+    kq[s] = 2 * duo + s;
+    okq[s] = item_ok && kq[s] < p.n_pairs;
+    bq[s] = okq[s] ? kq[s] / p.grp : 0;
+    len[s] = okq[s] ? min(max(p.seq_lens[bq[s]], 0), p.max_seq_len) : 0;
+  }
+  const int p0 = ch * p.Lc;
+  const int lenx = max(len[0], len[1]);
+  const bool active = item_ok && p0 < lenx;   // wave-uniform
+
+  float m[2] = {-INFINITY, -INFINITY};   // running max (log2 domain)
+  float l[2] = {0.f, 0.f};               // sum of the rounded p used in the products
+  float lx[2] = {0.f, 0.f};              // exact sum of p (for the logsumexp)
+  float4v acc[2][U];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[s][u] = (float4v){0.f, 0.f, 0.f, 0.f};
 
   if (active) {
-    // ---- K-side A operands: for frequency pair j, lane lb supplies row lb of
-    //      [[q_f, q_h, 0, 0], [q_h, -q_f, 0, 0], [0, 0, q_f', q_h'], [0, 0, q_h', -q_f']]
-    //      (f = 2j, f' = 2j+1 of quarter la; q_h = q_{f + D/2}), so the MFMA
-    //      yields X_f, Y_f, X_f', Y_f' of the position in each column.
-    half4v AK[FP];
-    half4v AKl[QF32 ? FP : 1];
+    // ---- K-side A operands.  For frequency f (the i-th of quarter la) lane lb
+    //      supplies row lb of the block-diagonal
+    //        [[q0_f, q0_h, 0, 0], [q0_h, -q0_f, 0, 0], [0, 0, q1_f, q1_h], [0, 0, q1_h, -q1_f]]
+    //      (q_h = q_{f + D/2}; pair 0 and pair 1 of the duo), so that with the
+    //      key column (k0_f, k0_h, k1_f, k1_h) of a position the MFMA yields
+    //      X0, Y0, X1, Y1 of that position.
+    half4v AK[F];
+    half4v AKl[QF32 ? F : 1];
     {
-      const size_t qoff = ((size_t)b * p.H_q + jq) * D + la * F;
+      const int s = lb >> 1;
+      const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
+      const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
+      const size_t qoff = ((size_t)bb * p.H_q + jq) * D + la * F;
 #pragma unroll
-      for (int j = 0; j < FP; ++j) {
-        const int f = 2 * j + (lb >> 1);     // rows 0,1 use f = 2j, rows 2,3 use 2j+1
+      for (int i = 0; i < F; ++i) {
         float a, c;
         if constexpr (QF32) {
-          a = ((const float*)p.q)[qoff + f];
-          c = ((const float*)p.q)[qoff + D / 2 + f];
+          a = ((const float*)p.q)[qoff + i];
+          c = ((const float*)p.q)[qoff + D / 2 + i];
         } else {
-          a = u2f((uint32_t)((const uint16_t*)p.q)[qoff + f] << 16);
-          c = u2f((uint32_t)((const uint16_t*)p.q)[qoff + D / 2 + f] << 16);
+          a = u2f((uint32_t)((const uint16_t*)p.q)[qoff + i] << 16);
+          c = u2f((uint32_t)((const uint16_t*)p.q)[qoff + D / 2 + i] << 16);
         }
         const float x0 = (lb & 1) ? c : a, x1 = (lb & 1) ? -a : c;
         const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
         const _Float16 z = (_Float16)0.f;
-        AK[j] = (lb >> 1) ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
+        AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
         if constexpr (QF32) {
           const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-          AKl[j] = (lb >> 1) ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
+          AKl[i] = s ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
         }
       }
     }
 
     // lane constants
-    const uint32_t koff = (uint32_t)(lane % NSLOT) * EB;   // K stripe window
-    const uint32_t voff = 128u + koff;                       // V stripe window
+    const uint32_t koff = (uint32_t)(lane % NSLOT) * EB;   // K stripe window in LDS
+    const uint32_t voff = 128u + koff;                       // V stripe window in LDS
     const uint32_t asel0 = lb == 0 ? 0x0c0c0100u : (lb == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
     const uint32_t asel1 = lb == 2 ? 0x0c0c0100u : (lb == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
     const int bperm_src = ((lane & 48) | (lb << 2) | la) << 2;  // K-role lane holding my V position
     const int P = 1 << p.log2P;
-    const size_t kv_stride = (size_t)P * R;                   // V rows follow the K rows of a page
-    const int32_t* btb = p.block_table + (size_t)b * p.max_pages;
-    const int NT = p.NT;
-    const int gbase = p0 + pgrp * 4;          // first position of this row's group at step 0
-    const int lim = min(len, p0 + p.Lc);
-    const int last = max(len - 1, 0);
-    int steps = lim > gbase ? (lim - gbase + NT - 1) / NT : 0;
+    const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
+    const size_t page_stride = (size_t)p.H_kv * 2 * kv_stride;
+    const uint8_t* head_base = p.cache + (size_t)h * 2 * kv_stride;
+    // byte offsets of the lane's K and V row quarters from the first row of
+    // its group: the whole step inside one page (SP), or the row's own 4
+    // positions (pages of 8 positions)
+    const uint32_t kro = (uint32_t)(((SP ? 4 * row : 0) + lb) * R + la * LB);
+    const uint32_t vro = kv_stride + (uint32_t)(((SP ? 4 * row : 0) + la) * R + lb * LB);
+    const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
+    int lim[2], last[2];
+    const int32_t* btb[2];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) steps = max(steps, __shfl_xor(steps, o));
-    steps = __builtin_amdgcn_readfirstlane((steps + 1) & ~1);   // two steps per iteration
+    for (int s = 0; s < 2; ++s) {
+      lim[s] = min(len[s], p0 + p.Lc);
+      last[s] = max(len[s] - 1, 0);
+      btb[s] = p.block_table + (size_t)bq[s] * p.max_pages;
+    }
+    const int limx = max(lim[0], lim[1]);
+    const int glast = (max(last[0], last[1]) >> 4) << 4;   // last step-aligned group with data
+    const int steps = ((limx - p0 + NT - 1) / NT + 1) & ~1;   // two steps per iteration
+    // an opaque zero: keeps the page-id loads on the vector path, in order
+    // with the row loads (scalar loads would share a counter with the LDS gathers)
+    const int vz = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
 
-    // raw block-table entry of the step's position group (only trusted when len > 0)
-    auto page_at = [&](int st) -> int {
-      const int gs = min(gbase + st * NT, last);
-      return btb[gs >> p.log2P];
+    // raw block-table entries of the step's pages, one per stream (only
+    // trusted when the stream's length is positive)
+    auto page_at = [&](int st, int* pg) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if constexpr (SP) pg[s] = btb[s][(min(p0 + st * NT, last[s]) >> p.log2P) + vz];
+        else pg[s] = btb[s][min(p0 + st * NT + 4 * row, last[s]) >> p.log2P];
+      }
     };
-    auto row_load = [&](int st, int raw_page, uint32_t* kw, uint32_t* vw) {
-      const int page = len > 0 ? raw_page : 0;
-      const int g0 = gbase + st * NT;
-      const int pk = min(g0 + lb, last), pv = min(g0 + la, last);
-      const uint8_t* base = p.cache + ((size_t)page * p.H_kv + h) * 2 * kv_stride;
-      RowLoad<LB>::load(base + (size_t)(pk & (P - 1)) * R + la * LB, kw);
-      RowLoad<LB>::load(base + kv_stride + (size_t)(pv & (P - 1)) * R + lb * LB, vw);
+    auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW]) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint8_t* base;
+        if constexpr (SP) {
+          const int page = len[s] > 0 ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
+          const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
+          base = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+        } else {
+          const int page = len[s] > 0 ? raw_page[s] : 0;
+          const int gs = min(p0 + st * NT + 4 * row, last[s]) & ~3;
+          base = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+        }
+        RowLoad<LB>::load(base + kro, kw[s]);
+        RowLoad<LB>::load(base + vro, vw[s]);
+      }
     };
     // table rows of positions 4g..4g+3 are interleaved: chunk j of quarter la
     // of position 4g + n sits at float4 ((g*FP + j)*4 + la)*4 + n, so the 16
     // lanes of a row (4 positions x 4 quarters) read one contiguous 256-B run
-    auto table_load = [&](int st, float4v* tb) {
-      const int pk = min(gbase + st * NT + lb, last);
-      const float4v* tr = (const float4v*)p.rope + ((size_t)(pk >> 2) * FP * 4 + la) * 4 + (pk & 3);
+    float4v tb[FP];
+    auto table_load = [&](int st) {
+      const int gt = min(p0 + st * NT, glast);
+      const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
 #pragma unroll
       for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
     };
 
-    // gathered K and V slice entries of the current step
-    Entry<EB> klo[Q], khi[Q], ve[2 * Q];
-    auto gather_k = [&](const uint32_t* kw) {
+    // gathered K and V slice entries of the current step, per stream
+    Entry<EB> klo[NS][Q], khi[NS][Q], ve[NS][2 * Q];
+    auto gather_k = [&](uint32_t (*kw)[LW]) {
 #pragma unroll
-      for (int r = 0; r < Q; ++r) {
-        klo[r] = lds_entry<EB>(lds, slot_addr<BITS>(kw, r, koff));
-        khi[r] = lds_entry<EB>(lds, slot_addr<BITS>(kw, Q + r, koff));
-      }
-    };
-    auto gather_v = [&](const uint32_t* vw) {
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int sl = 0; sl < 2 * Q; ++sl) ve[sl] = lds_entry<EB>(lds, slot_addr<BITS>(vw, sl, voff));
-    };
-
-    // one decode step.  On entry klo/khi/ve hold the gathers of step st and
-    // (kwn, vwn) the index rows of step st+1.  The step gathers step st+1 as
-    // soon as the registers free up, then refills (kwn, vwn) with the rows of
-    // st+3 (page id pgr, read two steps earlier) and reads the page of st+5.
-    // tcur holds the RoPE rows of st; tnext receives those of st+1.
-    auto do_step = [&](int st, uint32_t* kwn, uint32_t* vwn, const float4v* tcur, float4v* tnext, int& pgr) {
-      const int g0 = gbase + st * NT;
-      table_load(st + 1, tnext);
-
-      // ---- K side: X, Y of every frequency pair on the matrix cores (all
-      //      issued back to back), then s = sum_f cos_f X_f + sin_f Y_f
-      float4v xy[FP];
-#pragma unroll
-      for (int j = 0; j < FP; ++j) {
-        const int r = (2 * j) / C, e = (2 * j) % C;          // entry and element of f = 2j
-        const uint32_t w0 = perm(khi[r].d[e >> 1], klo[r].d[e >> 1], 0x05040100u);   // (k_f,  k_h)
-        const uint32_t w1 = perm(khi[r].d[e >> 1], klo[r].d[e >> 1], 0x07060302u);   // (k_f', k_h')
-        const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
-        xy[j] = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[j], Bk, (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        if constexpr (QF32) xy[j] = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[j], Bk, xy[j], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, QF32 ? 2 * FP : FP, 0);   // the MFMAs first
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < FP; ++j) {
-        const float4v t4 = tcur[j];
-        s0 = fmaf(t4.x, xy[j].x, s0);
-        s1 = fmaf(t4.y, xy[j].y, s1);
-        s0 = fmaf(t4.z, xy[j].z, s0);
-        s1 = fmaf(t4.w, xy[j].w, s1);
-      }
-      float s = s0 + s1;
-      // sum over the four quarters (lanes 4 apart within the 16-lane row)
-      s += u2f(__builtin_amdgcn_mov_dpp(f2u(s), 0x124, 0xf, 0xf, true));   // row_ror:4
-      s += u2f(__builtin_amdgcn_mov_dpp(f2u(s), 0x128, 0xf, 0xf, true));   // row_ror:8
-      // to the V role: this lane handles position slot la
-      s = u2f(__builtin_amdgcn_ds_bpermute(bperm_src, f2u(s)));
-      gather_k(kwn);                                  // K entries of step st+1
-      const bool valid = g0 + la < lim;
-
-      // ---- online softmax (log2 domain, lazy max)
-      const float s2 = valid ? s * p.scale_log2 : -INFINITY;
-      const bool need = s2 > m + LAZY_TAU;
-      if (__ballot(need) != 0) {
-        if (need) {
-          const float fct = __builtin_amdgcn_exp2f(m - s2);
-          l *= fct;
-          lx *= fct;
-#pragma unroll
-          for (int u = 0; u < U; ++u) acc[u] *= fct;
-          m = s2;
+        for (int r = 0; r < Q; ++r) {
+          klo[s][r] = lds_entry<EB>(lds, slot_addr<BITS>(kw[s], r, koff));
+          khi[s][r] = lds_entry<EB>(lds, slot_addr<BITS>(kw[s], Q + r, koff));
         }
+    };
+    auto gather_v = [&](uint32_t (*vw)[LW]) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int sl = 0; sl < 2 * Q; ++sl) ve[s][sl] = lds_entry<EB>(lds, slot_addr<BITS>(vw[s], sl, voff));
+    };
+
+    // one decode step.  On entry klo/khi/ve hold the gathers of step st, tb
+    // the RoPE rows of st, and (kwn, vwn) the index rows of step st+1.  The
+    // step reloads tb for st+1 and gathers step st+1 as soon as the registers
+    // free up, then refills (kwn, vwn) with the rows of st+3 (page ids pgr,
+    // read two steps earlier) and reads the pages of st+5.
+    auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], int* pgr) {
+      const int g0 = p0 + st * NT;
+
+      // ---- K side: X, Y of both pairs for every frequency on the matrix
+      //      cores, then s = sum_f cos_f X_f + sin_f Y_f in fp32
+      float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        const int r = i / C, e = i % C;                      // entry and element of frequency i
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
+        const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
+        const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
+        float4v xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
+        const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
+        const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
+        sa0 = fmaf(cs, xy.x, sa0);
+        sb0 = fmaf(sn, xy.y, sb0);
+        sa1 = fmaf(cs, xy.z, sa1);
+        sb1 = fmaf(sn, xy.w, sb1);
       }
-      const float pf = valid ? __builtin_amdgcn_exp2f(s2 - m) : 0.f;
-      lx += pf;
-      const _Float16 ph = (_Float16)pf;
-      const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
-      const half4v A = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
-      // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
-      half4v Alo;
-      if constexpr (QF32) {
-        const _Float16 pl = (_Float16)(pf - (float)ph);
-        const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
-        Alo = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
-        l += (float)ph + (float)pl;
-      } else {
-        l += (float)ph;
+      table_load(st + 1);                               // RoPE rows of step st+1
+      float sc[2] = {sa0 + sb0, sa1 + sb1};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // sum over the four quarters (lanes 4 apart within the 16-lane row)
+        float v = sc[s];
+        v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x124, 0xf, 0xf, true));   // row_ror:4
+        v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x128, 0xf, 0xf, true));   // row_ror:8
+        // to the V role: this lane handles position slot la
+        sc[s] = u2f(__builtin_amdgcn_ds_bpermute(bperm_src, f2u(v)));
+      }
+      gather_k(kwn);                                  // K entries of step st+1
+
+      // ---- online softmax per pair (log2 domain, lazy max)
+      const int pos = g0 + 4 * row + la;
+      half4v A[2], Alo[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bool valid = pos < lim[s];
+        const float s2 = valid ? sc[s] * p.scale_log2 : -INFINITY;
+        const bool need = s2 > m[s] + LAZY_TAU;
+        if (__ballot(need) != 0) {
+          if (need) {
+            const float fct = __builtin_amdgcn_exp2f(m[s] - s2);
+            l[s] *= fct;
+            lx[s] *= fct;
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[s][u] *= fct;
+            m[s] = s2;
+          }
+        }
+        const float pf = valid ? __builtin_amdgcn_exp2f(s2 - m[s]) : 0.f;
+        lx[s] += pf;
+        const _Float16 ph = (_Float16)pf;
+        const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
+        A[s] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
+        // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
+        if constexpr (QF32) {
+          const _Float16 pl = (_Float16)(pf - (float)ph);
+          const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
+          Alo[s] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
+          l[s] += (float)ph + (float)pl;
+        } else {
+          l[s] += (float)ph;
+        }
       }
 
       // ---- V side: acc += p * v on the matrix cores (block = one token)
 #pragma unroll
-      for (int sl = 0; sl < 2 * Q; ++sl) {
-        if constexpr (EB == 8) {
-          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[sl].d[0], ve[sl].d[1]});
-          acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bv, acc[sl], 0, 0, 0);
-          if constexpr (QF32) acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo, Bv, acc[sl], 0, 0, 0);
-        } else if constexpr (EB == 16) {
-          const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[sl].d[0], ve[sl].d[1]});
-          const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[sl].d[2], ve[sl].d[3]});
-          acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, B0, acc[2 * sl], 0, 0, 0);
-          if constexpr (QF32) acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo, B0, acc[2 * sl], 0, 0, 0);
-          acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, B1, acc[2 * sl + 1], 0, 0, 0);
-          if constexpr (QF32) acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo, B1, acc[2 * sl + 1], 0, 0, 0);
-        } else if (sl & 1) {
-          // two 2-channel entries form one 4-channel unit
-          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[sl - 1].d[0], ve[sl].d[0]});
-          acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bv, acc[sl >> 1], 0, 0, 0);
-          if constexpr (QF32) acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo, Bv, acc[sl >> 1], 0, 0, 0);
+      for (int s = 0; s < 2; ++s) {
+        const int sv = SHARE ? 0 : s;
+#pragma unroll
+        for (int sl = 0; sl < 2 * Q; ++sl) {
+          if constexpr (EB == 8) {
+            const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl].d[0], ve[sv][sl].d[1]});
+            acc[s][sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], Bv, acc[s][sl], 0, 0, 0);
+            if constexpr (QF32) acc[s][sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], Bv, acc[s][sl], 0, 0, 0);
+          } else if constexpr (EB == 16) {
+            const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl].d[0], ve[sv][sl].d[1]});
+            const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl].d[2], ve[sv][sl].d[3]});
+            acc[s][2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], B0, acc[s][2 * sl], 0, 0, 0);
+            if constexpr (QF32) acc[s][2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], B0, acc[s][2 * sl], 0, 0, 0);
+            acc[s][2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], B1, acc[s][2 * sl + 1], 0, 0, 0);
+            if constexpr (QF32) acc[s][2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], B1, acc[s][2 * sl + 1], 0, 0, 0);
+          } else if (sl & 1) {
+            // two 2-channel entries form one 4-channel unit
+            const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl - 1].d[0], ve[sv][sl].d[0]});
+            acc[s][sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], Bv, acc[s][sl >> 1], 0, 0, 0);
+            if constexpr (QF32) acc[s][sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], Bv, acc[s][sl >> 1], 0, 0, 0);
+          }
         }
       }
       gather_v(vwn);                                  // V entries of step st+1
       row_load(st + 3, pgr, kwn, vwn);
-      pgr = page_at(st + 5);
+      page_at(st + 5, pgr);
     };
 
-    uint32_t kwA[LW], vwA[LW], kwB[LW], vwB[LW];
-    float4v tbA[FP], tbB[FP];
-    row_load(0, page_at(0), kwA, vwA);
-    row_load(1, page_at(1), kwB, vwB);
-    table_load(0, tbA);
+    uint32_t kwA[NS][LW], vwA[NS][LW], kwB[NS][LW], vwB[NS][LW];
+    int pgA[NS], pgB[NS], pg0[NS];
+    page_at(0, pg0);
+    row_load(0, pg0, kwA, vwA);
+    page_at(1, pg0);
+    row_load(1, pg0, kwB, vwB);
+    table_load(0);
     gather_k(kwA);
     gather_v(vwA);
-    row_load(2, page_at(2), kwA, vwA);
-    int pgB = page_at(3), pgA = page_at(4);
+    page_at(2, pg0);
+    row_load(2, pg0, kwA, vwA);
+    page_at(3, pgB);
+    page_at(4, pgA);
     // an active wave has steps >= 2; the first two steps are peeled so that the
     // loads outstanding at the loop head are in the same order on entry and on
     // the back edge (the wait counts at the head are then tight)
-    do_step(0, kwB, vwB, tbA, tbB, pgB);
-    do_step(1, kwA, vwA, tbB, tbA, pgA);
+    do_step(0, kwB, vwB, pgB);
+    do_step(1, kwA, vwA, pgA);
     for (int st = 2; st < steps; st += 2) {
-      do_step(st, kwB, vwB, tbA, tbB, pgB);
-      do_step(st + 1, kwA, vwA, tbB, tbA, pgA);
+      do_step(st, kwB, vwB, pgB);
+      do_step(st + 1, kwA, vwA, pgA);
     }
   }
 
-  // ---- merge the position slots of each (pair, quarter) and write the chunk's partial
+  // ---- merge the 16 position slots of each (pair, quarter) and write the
+  //      chunk's partials, one pair of the duo at a time
   __syncthreads();                       // every wave is done with the slices
   float* red = (float*)lds + (size_t)wave * 64 * SW;
-  {
-    float* r = red + lane * SW;
 #pragma unroll
-    for (int u = 0; u < U; ++u) { r[4 * u] = acc[u].x; r[4 * u + 1] = acc[u].y; r[4 * u + 2] = acc[u].z; r[4 * u + 3] = acc[u].w; }
-    r[4 * U] = m;
-    r[4 * U + 1] = l;
-    r[4 * U + 2] = lx;
-  }
-  __syncthreads();
-  // one lane per (pair, quarter): row kslot < NP, position slot la == 0
-  if (active && pair_ok && kslot < p.NP && la == 0 && p0 < len) {
-    const int nsrc = 4 / p.NP * 4;       // rows of this pair x position slots
-    float M = -INFINITY;
-    for (int i = 0; i < nsrc; ++i) {
-      const int src = (kslot + (i >> 2) * p.NP) * 16 + (i & 3) * 4 + lb;
-      const float* r = red + src * SW;
-      if (r[4 * U + 1] > 0.f) M = fmaxf(M, r[4 * U]);
-    }
-    float4v o[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) o[u] = (float4v){0.f, 0.f, 0.f, 0.f};
-    float L = 0.f, LX = 0.f;
-    for (int i = 0; i < nsrc; ++i) {
-      const int src = (kslot + (i >> 2) * p.NP) * 16 + (i & 3) * 4 + lb;
-      const float* r = red + src * SW;
-      if (!(r[4 * U + 1] > 0.f)) continue;
-      const float wt = __builtin_amdgcn_exp2f(r[4 * U] - M);
+  for (int s = 0; s < 2; ++s) {
+    {
+      float* r = red + lane * SW;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        o[u].x = fmaf(wt, r[4 * u], o[u].x);
-        o[u].y = fmaf(wt, r[4 * u + 1], o[u].y);
-        o[u].z = fmaf(wt, r[4 * u + 2], o[u].z);
-        o[u].w = fmaf(wt, r[4 * u + 3], o[u].w);
+        r[4 * u] = acc[s][u].x; r[4 * u + 1] = acc[s][u].y; r[4 * u + 2] = acc[s][u].z; r[4 * u + 3] = acc[s][u].w;
       }
-      L = fmaf(wt, r[4 * U + 1], L);
-      LX = fmaf(wt, r[4 * U + 2], LX);
+      r[4 * U] = m[s];
+      r[4 * U + 1] = l[s];
+      r[4 * U + 2] = lx[s];
     }
-    const size_t part = (size_t)(h * p.n_pairs + k) * p.n_chunks + ch;
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float* op = p.part_o + part * D;
+    __syncthreads();
+    // one lane per quarter: row 0, position slot la == 0
+    if (active && okq[s] && row == 0 && la == 0 && p0 < len[s]) {
+      float M = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const float* r = red + (i * 4 + lb) * SW;
+        if (r[4 * U + 1] > 0.f) M = fmaxf(M, r[4 * U]);
+      }
+      float4v o[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int lc = 4 * u;
-      const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
-      *(float4v*)(op + base) = o[u] * inv;
+      for (int u = 0; u < U; ++u) o[u] = (float4v){0.f, 0.f, 0.f, 0.f};
+      float L = 0.f, LX = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const float* r = red + (i * 4 + lb) * SW;
+        if (!(r[4 * U + 1] > 0.f)) continue;
+        const float wt = __builtin_amdgcn_exp2f(r[4 * U] - M);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          o[u].x = fmaf(wt, r[4 * u], o[u].x);
+          o[u].y = fmaf(wt, r[4 * u + 1], o[u].y);
+          o[u].z = fmaf(wt, r[4 * u + 2], o[u].z);
+          o[u].w = fmaf(wt, r[4 * u + 3], o[u].w);
+        }
+        L = fmaf(wt, r[4 * U + 1], L);
+        LX = fmaf(wt, r[4 * U + 2], LX);
+      }
+      const size_t part = (size_t)(h * p.n_pairs + kq[s]) * p.n_chunks + ch;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      float* op = p.part_o + part * D;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int lc = 4 * u;
+        const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
+        *(float4v*)(op + base) = o[u] * inv;
+      }
+      if (lb == 0) p.part_lse[part] = L > 0.f ? M + log2f(LX) : -INFINITY;
     }
-    if (lb == 0) p.part_lse[part] = L > 0.f ? M + log2f(LX) : -INFINITY;
+    __syncthreads();
   }
 }
 
@@ -453,10 +518,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------- dispatch
+template <int D, int C, int BITS, bool QF32, bool SHARE>
+static void launch_split_sp(const DecodeParams& p, int grid, hipStream_t s) {
+  // a step's 16 positions lie in one page when pages hold at least 16 positions
+  if (p.log2P >= 4) hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true>), dim3(grid), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false>), dim3(grid), dim3(256), 0, s, p);
+}
+
 template <int D, int C, int BITS>
 static hipError_t launch_split_t(const DecodeParams& p, bool qf32, int grid, hipStream_t s) {
-  if (qf32) hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, true>), dim3(grid), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false>), dim3(grid), dim3(256), 0, s, p);
+  // pairs 2i and 2i+1 belong to one request when the GQA group size is even
+  const bool share = (p.grp & 1) == 0;
+  if (qf32) {
+    if (share) launch_split_sp<D, C, BITS, true, true>(p, grid, s);
+    else launch_split_sp<D, C, BITS, true, false>(p, grid, s);
+  } else {
+    if (share) launch_split_sp<D, C, BITS, false, true>(p, grid, s);
+    else launch_split_sp<D, C, BITS, false, false>(p, grid, s);
+  }
   return hipGetLastError();
 }
 

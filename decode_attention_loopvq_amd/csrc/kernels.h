@@ -18,11 +18,10 @@ struct DecodeParams {
   float* part_lse;            // [H_kv][n_pairs][n_chunks], log2 domain
   int B, H_kv, H_q, grp, max_pages, log2P;
   int n_pairs;                // B * grp (request, query head) pairs per KV head
-  int NP, NT;                 // pairs per wave (1, 2 or 4) and positions per wave step (16 / NP)
-  int n_pg;                   // pair groups per KV head
-  int Lc;                     // positions per chunk (one wave), a multiple of 2 * NT
+  int n_dg;                   // duos (pairs 2i, 2i+1) per KV head; one wave serves one duo
+  int Lc;                     // positions per chunk (one wave), a multiple of 32
   int n_chunks;
-  int items_per_head;         // n_pg * n_chunks wave work items per KV head
+  int items_per_head;         // n_dg * n_chunks wave work items per KV head
   int wg_per_head;            // ceil(items_per_head / 4)
   int max_seq_len;            // host bound; seq_lens are clamped to it
   float scale_log2;           // sm_scale * log2(e)

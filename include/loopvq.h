@@ -106,13 +106,14 @@ int loopvq_build_codebook_slices(const loopvq_dims* dims, const void* cb,
 
 /*
  * Host-side RoPE coefficient table in the layout the decode kernel streams.
- * Positions are taken in groups of four (the table is padded to
- * 4*ceil(max_pos/4) positions); for position p = 4g + n, chunk j < D/16 and
+ * The table is padded to 16*ceil(max_pos/16) positions (the decode kernel
+ * reads 16 positions per step); for position p = 4g + n, chunk j < D/16 and
  * lane quarter i < 4, the four floats at (((g*(D/16) + j)*4 + i)*4 + n)*4 are
  *     cos(p*theta_f), sin(p*theta_f), cos(p*theta_{f+1}), sin(p*theta_{f+1})
  * with f = i*(D/8) + 2*j and theta_f = base^(-2f/D), computed in fp64 and
- * rounded to fp32.  [LoopVQ paper, App. C: the kernel reads cos/sin from a
- * table precomputed for all positions instead of evaluating transcendentals.]
+ * rounded to fp32.  [LoopVQ paper, appendix "Optimizing pre-RoPE vector
+ * quantization serving efficiency": the kernel reads cos/sin from a table
+ * precomputed for all positions instead of evaluating transcendentals.]
  *   table [host] must hold loopvq_rope_table_floats(max_pos, D) floats.  The
  *   caller copies it to the device once.
  */

@@ -131,7 +131,7 @@ def test_workspace_bytes_monotone(L):
 @pytest.mark.parametrize("D,max_pos", [(64, 40001), (128, 40000)])
 def test_rope_table_matches_oracle(L, D, max_pos):
     t = L.loopvq_rope_table(max_pos, D).numpy()
-    padded = (max_pos + 3) // 4 * 4
+    padded = (max_pos + 15) // 16 * 16
     assert t.size == padded * D == L.lib().loopvq_rope_table_floats(max_pos, D)
     # [position group][chunk j][quarter i][position in group][cos f, sin f, cos f+1, sin f+1]
     t = t.reshape(padded // 4, D // 16, 4, 4, 4).transpose(0, 3, 1, 2, 4).reshape(padded, D // 16, 4, 4)
