@@ -40,12 +40,12 @@ int check_dims(const loopvq_dims* d) {
 }
 
 struct DecodePlan {
-  int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid;
+  int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid, shared_rope;
   size_t n_part, bytes_o, bytes_lse;
 };
 
 // A wave serves one duo of (request, query head) pairs (2i, 2i+1) over one
-// chunk of Lc positions, NT = 16 consecutive positions per step; the four
+// chunk of Lc positions, NT = 16 consecutive positions per step; the eight
 // waves of a workgroup share a KV head (and its LDS slices).
 DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   DecodePlan pl{};
@@ -54,17 +54,22 @@ DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   pl.NT = 16;
   pl.n_dg = std::max(1, (pl.n_pairs + 1) / 2);
   const long long len = std::max(max_seq_len, 1);
-  // about 2048 waves (8 per CU) over the whole call
+  // workgroup-shared RoPE rows: the eight waves of a workgroup must hold eight
+  // duos of one chunk (pages of >= 16 positions, bf16 queries)
+  pl.shared_rope = pl.n_dg % 8 == 0 && d->page_size >= 16 && d->io_dtype == LOOPVQ_DTYPE_BF16;
   const long long work = (long long)d->H_kv * pl.n_dg * len;
-  const long long step2 = 2LL * pl.NT;
+  const long long step2 = (pl.shared_rope ? 6LL : 2LL) * pl.NT;   // steps per loop iteration
+  // about 2048 waves (8 per CU) over the whole call
   long long Lc = (work + 2047) / 2048;
   Lc = (Lc + step2 - 1) / step2 * step2;
+  // shared rows keep each chunk's page ids in a 128-entry list per stream
+  if (pl.shared_rope) Lc = std::min(Lc, (126LL * d->page_size) / step2 * step2);
   Lc = std::max(Lc, step2);
   Lc = std::min(Lc, (len + step2 - 1) / step2 * step2);
   pl.Lc = (int)Lc;
   pl.n_chunks = (int)((len + pl.Lc - 1) / pl.Lc);
   pl.items_per_head = pl.n_dg * pl.n_chunks;
-  pl.wg_per_head = (pl.items_per_head + 3) / 4;
+  pl.wg_per_head = (pl.items_per_head + 7) / 8;   // eight waves per workgroup
   pl.grid = d->H_kv * pl.wg_per_head;
   pl.n_part = (size_t)d->H_kv * std::max(pl.n_pairs, 1) * pl.n_chunks;
   pl.bytes_o = align256(pl.n_part * d->D * sizeof(float));
@@ -221,6 +226,7 @@ int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const voi
   p.log2P = ilog2(dims->page_size);
   p.n_pairs = pl.n_pairs;
   p.n_dg = pl.n_dg;
+  p.shared_rope = pl.shared_rope;
   p.Lc = pl.Lc;
   p.n_chunks = pl.n_chunks;
   p.items_per_head = pl.items_per_head;

@@ -57,8 +57,8 @@ template <> struct RowLoad<16> { static __device__ __forceinline__ void load(con
 template <int BITS>
 __device__ __forceinline__ uint32_t slot_addr(const uint32_t* w, int s, uint32_t lane_off) {
   if constexpr (BITS == 8) {
-    // byte 1 <- code, byte 0 <- lane offset, bytes 2,3 <- 0
-    return perm(w[s >> 2], lane_off, 0x0c0c0000u | ((4u + (s & 3)) << 8));
+    // byte 1 <- code; bytes 0 and 2 <- lane offset (window, K|V region); byte 3 <- 0
+    return perm(w[s >> 2], lane_off, 0x0c020000u | ((4u + (s & 3)) << 8));
   } else {
     uint32_t code = (w[s >> 3] >> ((s & 7) * 4)) & 15u;
     return (code << 8) | lane_off;
@@ -81,14 +81,14 @@ __device__ __forceinline__ Entry<EB> lds_entry(const uint8_t* lds, uint32_t addr
   return e;
 }
 
-template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP, bool ST>
+__global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   constexpr int N = D / C;            // groups per row
   constexpr int Q = N / 8;            // lo (and hi) groups per lane quarter
   constexpr int F = D / 8;            // RoPE frequencies per lane quarter (one K MFMA each)
   constexpr int FP = F / 2;           // float4 table words per quarter (two frequencies each)
   constexpr int EB = 2 * C;           // bytes of one slice entry
-  constexpr int NSLOT = 128 / EB;     // bank windows per 128-byte LDS stripe
+  constexpr int NWIN = 256 / EB;      // bank windows per 256-byte LDS row (64 banks)
   constexpr int R = N * BITS / 8;     // row bytes
   constexpr int LB = R / 4;           // row bytes per lane quarter
   constexpr int LW = (LB + 3) / 4;    // row words per lane
@@ -97,11 +97,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   constexpr int NS = SHARE ? 1 : 2;   // index streams per wave: the duo's requests
   constexpr int NT = 16;              // positions per wave step
   constexpr int SW = 4 * U + 3;       // floats of one lane's softmax state (one pair)
-  constexpr int LDS_SLICES = KENT * 256;
-  constexpr int LDS_MERGE = 4 * 64 * SW * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_SLICES > LDS_MERGE ? LDS_SLICES : LDS_MERGE];
+  constexpr int WAVES = 8;            // waves per workgroup, all on one KV head
+  constexpr int TSTEP = NT * D * 4;   // bytes of the RoPE rows of one step
+  constexpr int LDS_SLICES = 2 * KENT * 256;
+  constexpr int LDS_RING = ST ? 2 * TSTEP : 0;
+  constexpr int PGMAX = 128;          // page-list entries per stream and wave (shared rows)
+  constexpr int LDS_PAGES = ST ? WAVES * 2 * PGMAX * 4 : 0;
+  constexpr int LDS_MERGE = WAVES * 64 * SW * 4;
+  constexpr int LDS_BYTES = LDS_SLICES + LDS_RING + LDS_PAGES > LDS_MERGE ? LDS_SLICES + LDS_RING + LDS_PAGES
+                                                                          : LDS_MERGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ int wsteps[WAVES];
 
-  // ---- workgroup -> (KV head, 4 work items).  Heads vary fastest, so each
+  // ---- workgroup -> (KV head, 8 work items).  Heads vary fastest, so each
   //      XCD (blocks of one residue mod 8, renumbered contiguously) owns a
   //      band of chunks of every head: its L2 holds only that band's RoPE rows.
   int bid = blockIdx.x;
@@ -110,12 +118,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   const int wgi = bid / p.H_kv;
   const int h = bid - wgi * p.H_kv;
 
-  // ---- stage the K and V slices of head h, replicated per bank window
+  // ---- stage the K and V slices of head h, each entry replicated over a
+  //      256-byte row (one copy per bank window): entry e of region kv sits
+  //      at kv*KENT*256 + e*256, and lane l reads window l % NWIN, so the
+  //      random gathers of a wave hit every bank once per pass
   {
     const uint8_t* src = (const uint8_t*)p.slices + (size_t)h * 2 * KENT * EB;
-    for (int x = threadIdx.x; x < KENT * 16; x += blockDim.x) {
-      const int e = x >> 4, kv = (x >> 3) & 1, cchunk = x & 7;
-      const uint8_t* sp = src + ((size_t)kv * KENT + e) * EB;
+    for (int x = threadIdx.x; x < 2 * KENT * 16; x += blockDim.x) {
+      const int ke = x >> 4, cchunk = x & 15;           // ke = kv * KENT + e
+      const uint8_t* sp = src + (size_t)ke * EB;
       uint4v v;
       if constexpr (EB == 16) {
         v = *(const uint4v*)sp;
@@ -124,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
       } else {
         uint32_t t = *(const uint32_t*)sp; v = (uint4v){t, t, t, t};
       }
-      *(uint4v*)(lds + e * 256 + kv * 128 + cchunk * 16) = v;
+      *(uint4v*)(lds + ke * 256 + cchunk * 16) = v;
     }
   }
   __syncthreads();
@@ -132,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   // ---- this wave's work item (wave-uniform): one duo of pairs, one chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int item = wgi * 4 + wave;
+  const int item = wgi * WAVES + wave;
   const bool item_ok = item < p.items_per_head;
   const int ch = item_ok ? item / p.n_dg : 0;
   const int duo = item_ok ? item - ch * p.n_dg : 0;
@@ -152,318 +163,462 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   const int lenx = max(len[0], len[1]);
   const bool active = item_ok && p0 < lenx;   // wave-uniform
 
-  float m[2] = {-INFINITY, -INFINITY};   // running max (log2 domain)
-  float l[2] = {0.f, 0.f};               // sum of the rounded p used in the products
-  float lx[2] = {0.f, 0.f};              // exact sum of p (for the logsumexp)
-  float4v acc[2][U];
+  // V role: rows 0-1 of the wave serve pair 0 and rows 2-3 pair 1; a lane
+  // takes position slot la of the step's groups 2*rp and 2*rp + 1 (positions
+  // 8*rp + la and 8*rp + 4 + la) and channel quarter lb
+  const int sv = row >> 1, rp = row & 1;
+  float m = -INFINITY;                   // running max (log2 domain)
+  float l = 0.f;                         // sum of the rounded p used in the products
+  float lx = 0.f;                        // exact sum of p (for the logsumexp)
+  float4v acc[U];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[s][u] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < U; ++u) acc[u] = (float4v){0.f, 0.f, 0.f, 0.f};
 
+  // ---- K-side A operands (read by active waves only).  For frequency f (the
+  //      i-th of quarter la) lane lb supplies row lb of the block-diagonal
+  //        [[q0_f, q0_h, 0, 0], [q0_h, -q0_f, 0, 0], [0, 0, q1_f, q1_h], [0, 0, q1_h, -q1_f]]
+  //      (q_h = q_{f + D/2}; pair 0 and pair 1 of the duo), so that with the
+  //      key column (k0_f, k0_h, k1_f, k1_h) of a position the MFMA yields
+  //      X0, Y0, X1, Y1 of that position.
+  half4v AK[F];
+  half4v AKl[QF32 ? F : 1];
   if (active) {
-    // ---- K-side A operands.  For frequency f (the i-th of quarter la) lane lb
-    //      supplies row lb of the block-diagonal
-    //        [[q0_f, q0_h, 0, 0], [q0_h, -q0_f, 0, 0], [0, 0, q1_f, q1_h], [0, 0, q1_h, -q1_f]]
-    //      (q_h = q_{f + D/2}; pair 0 and pair 1 of the duo), so that with the
-    //      key column (k0_f, k0_h, k1_f, k1_h) of a position the MFMA yields
-    //      X0, Y0, X1, Y1 of that position.
-    half4v AK[F];
-    half4v AKl[QF32 ? F : 1];
-    {
-      const int s = lb >> 1;
-      const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
-      const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
-      const size_t qoff = ((size_t)bb * p.H_q + jq) * D + la * F;
+    const int s = lb >> 1;
+    const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
+    const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
+    const size_t qoff = ((size_t)bb * p.H_q + jq) * D + la * F;
 #pragma unroll
-      for (int i = 0; i < F; ++i) {
-        float a, c;
-        if constexpr (QF32) {
-          a = ((const float*)p.q)[qoff + i];
-          c = ((const float*)p.q)[qoff + D / 2 + i];
-        } else {
-          a = u2f((uint32_t)((const uint16_t*)p.q)[qoff + i] << 16);
-          c = u2f((uint32_t)((const uint16_t*)p.q)[qoff + D / 2 + i] << 16);
-        }
-        const float x0 = (lb & 1) ? c : a, x1 = (lb & 1) ? -a : c;
-        const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-        const _Float16 z = (_Float16)0.f;
-        AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
-        if constexpr (QF32) {
-          const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-          AKl[i] = s ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
-        }
+    for (int i = 0; i < F; ++i) {
+      float a, c;
+      if constexpr (QF32) {
+        a = ((const float*)p.q)[qoff + i];
+        c = ((const float*)p.q)[qoff + D / 2 + i];
+      } else {
+        a = u2f((uint32_t)((const uint16_t*)p.q)[qoff + i] << 16);
+        c = u2f((uint32_t)((const uint16_t*)p.q)[qoff + D / 2 + i] << 16);
       }
-    }
-
-    // lane constants
-    const uint32_t koff = (uint32_t)(lane % NSLOT) * EB;   // K stripe window in LDS
-    const uint32_t voff = 128u + koff;                       // V stripe window in LDS
-    const uint32_t asel0 = lb == 0 ? 0x0c0c0100u : (lb == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
-    const uint32_t asel1 = lb == 2 ? 0x0c0c0100u : (lb == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
-    const int bperm_src = ((lane & 48) | (lb << 2) | la) << 2;  // K-role lane holding my V position
-    const int P = 1 << p.log2P;
-    const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
-    const size_t page_stride = (size_t)p.H_kv * 2 * kv_stride;
-    const uint8_t* head_base = p.cache + (size_t)h * 2 * kv_stride;
-    // byte offsets of the lane's K and V row quarters from the first row of
-    // its group: the whole step inside one page (SP), or the row's own 4
-    // positions (pages of 8 positions)
-    const uint32_t kro = (uint32_t)(((SP ? 4 * row : 0) + lb) * R + la * LB);
-    const uint32_t vro = kv_stride + (uint32_t)(((SP ? 4 * row : 0) + la) * R + lb * LB);
-    const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
-    int lim[2], last[2];
-    const int32_t* btb[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      lim[s] = min(len[s], p0 + p.Lc);
-      last[s] = max(len[s] - 1, 0);
-      btb[s] = p.block_table + (size_t)bq[s] * p.max_pages;
-    }
-    const int limx = max(lim[0], lim[1]);
-    const int glast = (max(last[0], last[1]) >> 4) << 4;   // last step-aligned group with data
-    const int steps = ((limx - p0 + NT - 1) / NT + 1) & ~1;   // two steps per iteration
-    // an opaque zero: keeps the page-id loads on the vector path, in order
-    // with the row loads (scalar loads would share a counter with the LDS gathers)
-    const int vz = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
-
-    // raw block-table entries of the step's pages, one per stream (only
-    // trusted when the stream's length is positive)
-    auto page_at = [&](int st, int* pg) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if constexpr (SP) pg[s] = btb[s][(min(p0 + st * NT, last[s]) >> p.log2P) + vz];
-        else pg[s] = btb[s][min(p0 + st * NT + 4 * row, last[s]) >> p.log2P];
+      const float x0 = (lb & 1) ? c : a, x1 = (lb & 1) ? -a : c;
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 z = (_Float16)0.f;
+      AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
+      if constexpr (QF32) {
+        const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+        AKl[i] = s ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
       }
-    };
-    auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW]) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint8_t* base;
-        if constexpr (SP) {
-          const int page = len[s] > 0 ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
-          const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
-          base = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
-        } else {
-          const int page = len[s] > 0 ? raw_page[s] : 0;
-          const int gs = min(p0 + st * NT + 4 * row, last[s]) & ~3;
-          base = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
-        }
-        RowLoad<LB>::load(base + kro, kw[s]);
-        RowLoad<LB>::load(base + vro, vw[s]);
-      }
-    };
-    // table rows of positions 4g..4g+3 are interleaved: chunk j of quarter la
-    // of position 4g + n sits at float4 ((g*FP + j)*4 + la)*4 + n, so the 16
-    // lanes of a row (4 positions x 4 quarters) read one contiguous 256-B run
-    float4v tb[FP];
-    auto table_load = [&](int st) {
-      const int gt = min(p0 + st * NT, glast);
-      const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
-#pragma unroll
-      for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
-    };
-
-    // gathered K and V slice entries of the current step, per stream
-    Entry<EB> klo[NS][Q], khi[NS][Q], ve[NS][2 * Q];
-    auto gather_k = [&](uint32_t (*kw)[LW]) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int r = 0; r < Q; ++r) {
-          klo[s][r] = lds_entry<EB>(lds, slot_addr<BITS>(kw[s], r, koff));
-          khi[s][r] = lds_entry<EB>(lds, slot_addr<BITS>(kw[s], Q + r, koff));
-        }
-    };
-    auto gather_v = [&](uint32_t (*vw)[LW]) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int sl = 0; sl < 2 * Q; ++sl) ve[s][sl] = lds_entry<EB>(lds, slot_addr<BITS>(vw[s], sl, voff));
-    };
-
-    // one decode step.  On entry klo/khi/ve hold the gathers of step st, tb
-    // the RoPE rows of st, and (kwn, vwn) the index rows of step st+1.  The
-    // step reloads tb for st+1 and gathers step st+1 as soon as the registers
-    // free up, then refills (kwn, vwn) with the rows of st+3 (page ids pgr,
-    // read two steps earlier) and reads the pages of st+5.
-    auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], int* pgr) {
-      const int g0 = p0 + st * NT;
-
-      // ---- K side: X, Y of both pairs for every frequency on the matrix
-      //      cores, then s = sum_f cos_f X_f + sin_f Y_f in fp32
-      float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < F; ++i) {
-        const int r = i / C, e = i % C;                      // entry and element of frequency i
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
-        const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
-        const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
-        float4v xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
-        const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
-        const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
-        sa0 = fmaf(cs, xy.x, sa0);
-        sb0 = fmaf(sn, xy.y, sb0);
-        sa1 = fmaf(cs, xy.z, sa1);
-        sb1 = fmaf(sn, xy.w, sb1);
-      }
-      table_load(st + 1);                               // RoPE rows of step st+1
-      float sc[2] = {sa0 + sb0, sa1 + sb1};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        // sum over the four quarters (lanes 4 apart within the 16-lane row)
-        float v = sc[s];
-        v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x124, 0xf, 0xf, true));   // row_ror:4
-        v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x128, 0xf, 0xf, true));   // row_ror:8
-        // to the V role: this lane handles position slot la
-        sc[s] = u2f(__builtin_amdgcn_ds_bpermute(bperm_src, f2u(v)));
-      }
-      gather_k(kwn);                                  // K entries of step st+1
-
-      // ---- online softmax per pair (log2 domain, lazy max)
-      const int pos = g0 + 4 * row + la;
-      half4v A[2], Alo[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bool valid = pos < lim[s];
-        const float s2 = valid ? sc[s] * p.scale_log2 : -INFINITY;
-        const bool need = s2 > m[s] + LAZY_TAU;
-        if (__ballot(need) != 0) {
-          if (need) {
-            const float fct = __builtin_amdgcn_exp2f(m[s] - s2);
-            l[s] *= fct;
-            lx[s] *= fct;
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[s][u] *= fct;
-            m[s] = s2;
-          }
-        }
-        const float pf = valid ? __builtin_amdgcn_exp2f(s2 - m[s]) : 0.f;
-        lx[s] += pf;
-        const _Float16 ph = (_Float16)pf;
-        const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
-        A[s] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
-        // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
-        if constexpr (QF32) {
-          const _Float16 pl = (_Float16)(pf - (float)ph);
-          const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
-          Alo[s] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
-          l[s] += (float)ph + (float)pl;
-        } else {
-          l[s] += (float)ph;
-        }
-      }
-
-      // ---- V side: acc += p * v on the matrix cores (block = one token)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int sv = SHARE ? 0 : s;
-#pragma unroll
-        for (int sl = 0; sl < 2 * Q; ++sl) {
-          if constexpr (EB == 8) {
-            const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl].d[0], ve[sv][sl].d[1]});
-            acc[s][sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], Bv, acc[s][sl], 0, 0, 0);
-            if constexpr (QF32) acc[s][sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], Bv, acc[s][sl], 0, 0, 0);
-          } else if constexpr (EB == 16) {
-            const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl].d[0], ve[sv][sl].d[1]});
-            const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl].d[2], ve[sv][sl].d[3]});
-            acc[s][2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], B0, acc[s][2 * sl], 0, 0, 0);
-            if constexpr (QF32) acc[s][2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], B0, acc[s][2 * sl], 0, 0, 0);
-            acc[s][2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], B1, acc[s][2 * sl + 1], 0, 0, 0);
-            if constexpr (QF32) acc[s][2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], B1, acc[s][2 * sl + 1], 0, 0, 0);
-          } else if (sl & 1) {
-            // two 2-channel entries form one 4-channel unit
-            const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[sv][sl - 1].d[0], ve[sv][sl].d[0]});
-            acc[s][sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[s], Bv, acc[s][sl >> 1], 0, 0, 0);
-            if constexpr (QF32) acc[s][sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[s], Bv, acc[s][sl >> 1], 0, 0, 0);
-          }
-        }
-      }
-      gather_v(vwn);                                  // V entries of step st+1
-      row_load(st + 3, pgr, kwn, vwn);
-      page_at(st + 5, pgr);
-    };
-
-    uint32_t kwA[NS][LW], vwA[NS][LW], kwB[NS][LW], vwB[NS][LW];
-    int pgA[NS], pgB[NS], pg0[NS];
-    page_at(0, pg0);
-    row_load(0, pg0, kwA, vwA);
-    page_at(1, pg0);
-    row_load(1, pg0, kwB, vwB);
-    table_load(0);
-    gather_k(kwA);
-    gather_v(vwA);
-    page_at(2, pg0);
-    row_load(2, pg0, kwA, vwA);
-    page_at(3, pgB);
-    page_at(4, pgA);
-    // an active wave has steps >= 2; the first two steps are peeled so that the
-    // loads outstanding at the loop head are in the same order on entry and on
-    // the back edge (the wait counts at the head are then tight)
-    do_step(0, kwB, vwB, pgB);
-    do_step(1, kwA, vwA, pgA);
-    for (int st = 2; st < steps; st += 2) {
-      do_step(st, kwB, vwB, pgB);
-      do_step(st + 1, kwA, vwA, pgA);
     }
   }
 
-  // ---- merge the 16 position slots of each (pair, quarter) and write the
-  //      chunk's partials, one pair of the duo at a time
-  __syncthreads();                       // every wave is done with the slices
-  float* red = (float*)lds + (size_t)wave * 64 * SW;
+  // ---- lane constants
+  const uint32_t koff = (uint32_t)(lane % NWIN) * EB;    // K window in LDS
+  const uint32_t voff = (uint32_t)(KENT * 256) + koff;     // V window in LDS
+  const uint32_t asel0 = lb == 0 ? 0x0c0c0100u : (lb == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
+  const uint32_t asel1 = lb == 2 ? 0x0c0c0100u : (lb == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
+  // K-role lanes holding my V positions: row 2*rp (+1), position slot la;
+  // quarters 2*sv, 2*sv + 1 expose pair sv's score after the quarter sum
+  const int bperm_a = ((32 * rp) | ((2 * sv + (lb & 1)) << 2) | la) << 2;
+  const int bperm_b = bperm_a + 64;
+  const int P = 1 << p.log2P;
+  const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
+  const size_t page_stride = (size_t)p.H_kv * 2 * kv_stride;
+  const uint8_t* head_base = p.cache + (size_t)h * 2 * kv_stride;
+  // byte offsets of the lane's K and V row quarters from the first row of
+  // its group: the whole step inside one page (SP), or the row's own 4
+  // positions (pages of 8 positions)
+  const uint32_t kro = (uint32_t)(((SP ? 4 * row : 0) + lb) * R + la * LB);
+  const uint32_t vro = kv_stride + (uint32_t)(((SP ? 8 * rp : 0) + la) * R + lb * LB);   // +4R: slot b
+  const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
+  int lim[2], last[2];
+  const int32_t* btb[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    {
-      float* r = red + lane * SW;
+    lim[s] = min(len[s], p0 + p.Lc);
+    last[s] = max(len[s] - 1, 0);
+    btb[s] = p.block_table + (size_t)bq[s] * p.max_pages;
+  }
+  const int limx = max(lim[0], lim[1]);
+  const int glast = (max(last[0], last[1]) >> 4) << 4;   // last step-aligned group with data
+  const int my_steps = active ? (limx - p0 + NT - 1) / NT : 0;   // wave-uniform
+  // an opaque zero: keeps the page-id loads on the vector path, in order
+  // with the row loads (scalar loads would share a counter with the LDS gathers)
+  const int vz = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
+
+  // raw block-table entries of the step's pages (only trusted when the
+  // stream's length is positive): one per stream with whole-step pages (SP);
+  // else per lane, one per stream for the K row group and one for the V groups
+  constexpr int NPG = SP ? NS : NS + 1;
+  auto page_at = [&](int st, int* pg) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        r[4 * u] = acc[s][u].x; r[4 * u + 1] = acc[s][u].y; r[4 * u + 2] = acc[s][u].z; r[4 * u + 3] = acc[s][u].w;
-      }
-      r[4 * U] = m[s];
-      r[4 * U + 1] = l[s];
-      r[4 * U + 2] = lx[s];
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (SP) pg[s] = btb[s][(min(p0 + st * NT, last[s]) >> p.log2P) + vz];
+      else pg[s] = btb[s][min(p0 + st * NT + 4 * row, last[s]) >> p.log2P];
     }
-    __syncthreads();
-    // one lane per quarter: row 0, position slot la == 0
-    if (active && okq[s] && row == 0 && la == 0 && p0 < len[s]) {
-      float M = -INFINITY;
-      for (int i = 0; i < 16; ++i) {
-        const float* r = red + (i * 4 + lb) * SW;
-        if (r[4 * U + 1] > 0.f) M = fmaxf(M, r[4 * U]);
+    if constexpr (!SP) pg[NS] = btb[sv][min(p0 + st * NT + 8 * rp, last[sv]) >> p.log2P];
+  };
+  // K rows of both streams at the lane's K position, V rows of stream sv at
+  // the lane's two V positions
+  auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW]) {
+    const uint8_t* vbase;
+    if constexpr (SP) {
+      const uint8_t* base[2];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int page = len[s] > 0 ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
+        const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
+        base[s] = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+        RowLoad<LB>::load(base[s] + kro, kw[s]);
       }
-      float4v o[U];
+      vbase = (NS == 1 || sv == 0) ? base[0] : base[NS - 1];
+    } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) o[u] = (float4v){0.f, 0.f, 0.f, 0.f};
-      float L = 0.f, LX = 0.f;
-      for (int i = 0; i < 16; ++i) {
-        const float* r = red + (i * 4 + lb) * SW;
-        if (!(r[4 * U + 1] > 0.f)) continue;
-        const float wt = __builtin_amdgcn_exp2f(r[4 * U] - M);
+      for (int s = 0; s < NS; ++s) {
+        const int page = len[s] > 0 ? raw_page[s] : 0;
+        const int gs = min(p0 + st * NT + 4 * row, last[s]) & ~3;
+        RowLoad<LB>::load(head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R + kro, kw[s]);
+      }
+      const int page = len[sv] > 0 ? raw_page[NS] : 0;
+      const int gs = min(p0 + st * NT + 8 * rp, last[sv]) & ~7;
+      vbase = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+    }
+    RowLoad<LB>::load(vbase + vro, vw[0]);
+    RowLoad<LB>::load(vbase + vro + 4 * R, vw[1]);
+  };
+  // table rows of positions 4g..4g+3 are interleaved: chunk j of quarter la
+  // of position 4g + n sits at float4 ((g*FP + j)*4 + la)*4 + n, so the 16
+  // lanes of a row (4 positions x 4 quarters) read one contiguous 256-B run,
+  // and the rows of one step form one contiguous TSTEP-byte block
+  float4v tb[FP];
+  auto table_load = [&](int st) {
+    const int gt = min(p0 + st * NT, glast);
+    const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          o[u].x = fmaf(wt, r[4 * u], o[u].x);
-          o[u].y = fmaf(wt, r[4 * u + 1], o[u].y);
-          o[u].z = fmaf(wt, r[4 * u + 2], o[u].z);
-          o[u].w = fmaf(wt, r[4 * u + 3], o[u].w);
+    for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
+  };
+
+  // gathered K slice entries per stream, V entries per V position slot
+  Entry<EB> klo[NS][Q], khi[NS][Q], ve[2][2 * Q];
+  auto gather_k = [&](uint32_t (*kw)[LW]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int r = 0; r < Q; ++r) {
+        klo[s][r] = lds_entry<EB>(lds, slot_addr<BITS>(kw[s], r, koff));
+        khi[s][r] = lds_entry<EB>(lds, slot_addr<BITS>(kw[s], Q + r, koff));
+      }
+  };
+  auto gather_v = [&](uint32_t (*vw)[LW]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int sl = 0; sl < 2 * Q; ++sl) ve[t][sl] = lds_entry<EB>(lds, slot_addr<BITS>(vw[t], sl, voff));
+  };
+
+  // ---- K side of a step: X, Y of both pairs for every frequency on the
+  //      matrix cores, then s = sum_f cos_f X_f + sin_f Y_f in fp32 (this
+  //      lane's quarter; klo/khi and tb hold the step's entries and rows)
+  auto k_side = [&](float* sc) {
+    float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      const int r = i / C, e = i % C;                      // entry and element of frequency i
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
+      const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
+      const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
+      float4v xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
+      const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
+      const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
+      sa0 = fmaf(cs, xy.x, sa0);
+      sb0 = fmaf(sn, xy.y, sb0);
+      sa1 = fmaf(cs, xy.z, sa1);
+      sb1 = fmaf(sn, xy.w, sb1);
+    }
+    // interleave: each MFMA is followed by VALU work (the next perms and this
+    // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QF32 ? 2 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    sc[0] = sa0 + sb0;
+    sc[1] = sa1 + sb1;
+  };
+  // sum over the four quarters (lanes 4 apart within the 16-lane row); lanes
+  // of quarters 0-1 then expose pair 0's score and quarters 2-3 pair 1's, and
+  // each V lane pulls its two positions of its pair
+  auto to_v_role = [&](const float* sc, float* sv2) {
+    float v0 = sc[0], v1 = sc[1];
+    v0 += u2f(__builtin_amdgcn_mov_dpp(f2u(v0), 0x124, 0xf, 0xf, true));   // row_ror:4
+    v1 += u2f(__builtin_amdgcn_mov_dpp(f2u(v1), 0x124, 0xf, 0xf, true));
+    v0 += u2f(__builtin_amdgcn_mov_dpp(f2u(v0), 0x128, 0xf, 0xf, true));   // row_ror:8
+    v1 += u2f(__builtin_amdgcn_mov_dpp(f2u(v1), 0x128, 0xf, 0xf, true));
+    const uint32_t ex = f2u(la >= 2 ? v1 : v0);
+    sv2[0] = u2f(__builtin_amdgcn_ds_bpermute(bperm_a, ex));
+    sv2[1] = u2f(__builtin_amdgcn_ds_bpermute(bperm_b, ex));
+  };
+  // ---- online softmax of pair sv at the lane's two positions (log2 domain,
+  //      lazy max) and the V side: acc += p * v on the matrix cores (block =
+  //      one token); p is rounded to fp16 for the product, and l adds the same
+  //      rounded p, so the output stays an exact convex combination
+  auto v_side = [&](int g0, const float* sv2) {
+    const int posa = g0 + 8 * rp + la;
+    const bool va = posa < lim[sv], vb = posa + 4 < lim[sv];
+    const float sa = va ? sv2[0] * p.scale_log2 : -INFINITY;
+    const float sb = vb ? sv2[1] * p.scale_log2 : -INFINITY;
+    const float smax = fmaxf(sa, sb);
+    const bool need = smax > m + LAZY_TAU;
+    if (__ballot(need) != 0) {
+      if (need) {
+        const float fct = __builtin_amdgcn_exp2f(m - smax);
+        l *= fct;
+        lx *= fct;
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] *= fct;
+        m = smax;
+      }
+    }
+    const float pa = va ? __builtin_amdgcn_exp2f(sa - m) : 0.f;
+    const float pb = vb ? __builtin_amdgcn_exp2f(sb - m) : 0.f;
+    lx += pa + pb;
+    half4v A[2], Alo[2];
+    const float pv[2] = {pa, pb};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const _Float16 ph = (_Float16)pv[t];
+      const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
+      A[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
+      // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
+      if constexpr (QF32) {
+        const _Float16 pl = (_Float16)(pv[t] - (float)ph);
+        const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
+        Alo[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
+        l += (float)ph + (float)pl;
+      } else {
+        l += (float)ph;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int sl = 0; sl < 2 * Q; ++sl) {
+        if constexpr (EB == 8) {
+          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
+          acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, acc[sl], 0, 0, 0);
+          if constexpr (QF32) acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, acc[sl], 0, 0, 0);
+        } else if constexpr (EB == 16) {
+          const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
+          const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[2], ve[t][sl].d[3]});
+          acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B0, acc[2 * sl], 0, 0, 0);
+          if constexpr (QF32) acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B0, acc[2 * sl], 0, 0, 0);
+          acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B1, acc[2 * sl + 1], 0, 0, 0);
+          if constexpr (QF32) acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B1, acc[2 * sl + 1], 0, 0, 0);
+        } else if (sl & 1) {
+          // two 2-channel entries form one 4-channel unit
+          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl - 1].d[0], ve[t][sl].d[0]});
+          acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, acc[sl >> 1], 0, 0, 0);
+          if constexpr (QF32) acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, acc[sl >> 1], 0, 0, 0);
         }
-        L = fmaf(wt, r[4 * U + 1], L);
-        LX = fmaf(wt, r[4 * U + 2], LX);
       }
-      const size_t part = (size_t)(h * p.n_pairs + kq[s]) * p.n_chunks + ch;
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      float* op = p.part_o + part * D;
+    }
+  };
+
+  if constexpr (!ST) {
+    // ================= per-wave RoPE rows (any batch shape)
+    if (active) {
+      const int steps = (my_steps + 1) & ~1;   // two steps per iteration
+      // one decode step.  On entry klo/khi/ve hold the gathers of step st, tb
+      // the RoPE rows of st, and (kwn, vwn) the index rows of step st+1.  The
+      // step reloads tb for st+1 and gathers step st+1 as soon as the
+      // registers free up, then refills (kwn, vwn) with the rows of st+3
+      // (page ids pgr, read two steps earlier) and reads the pages of st+5.
+      auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], int* pgr) {
+        float sc[2], sv2[2];
+        k_side(sc);
+        table_load(st + 1);                             // RoPE rows of step st+1
+        to_v_role(sc, sv2);
+        gather_k(kwn);                                  // K entries of step st+1
+        v_side(p0 + st * NT, sv2);
+        gather_v(vwn);                                  // V entries of step st+1
+        row_load(st + 3, pgr, kwn, vwn);
+        page_at(st + 5, pgr);
+      };
+      uint32_t kwA[NS][LW], vwA[2][LW], kwB[NS][LW], vwB[2][LW];
+      int pgA[NPG], pgB[NPG], pg0[NPG];
+      page_at(0, pg0);
+      row_load(0, pg0, kwA, vwA);
+      page_at(1, pg0);
+      row_load(1, pg0, kwB, vwB);
+      table_load(0);
+      gather_k(kwA);
+      gather_v(vwA);
+      page_at(2, pg0);
+      row_load(2, pg0, kwA, vwA);
+      page_at(3, pgB);
+      page_at(4, pgA);
+      // an active wave has steps >= 2; the first two steps are peeled so that
+      // the loads outstanding at the loop head are in the same order on entry
+      // and on the back edge (the wait counts at the head are then tight)
+      do_step(0, kwB, vwB, pgB);
+      do_step(1, kwA, vwA, pgA);
+      for (int st = 2; st < steps; st += 2) {
+        do_step(st, kwB, vwB, pgB);
+        do_step(st + 1, kwA, vwA, pgA);
+      }
+    }
+  } else {
+    // ================= RoPE rows shared by the workgroup.  The eight waves
+    // work on one chunk (eight duos of one head), so each step's TSTEP bytes
+    // of rows are fetched once per workgroup, one 16-byte piece per lane of
+    // each wave, into a two-slot LDS ring, and read back by every wave.  The
+    // workgroup moves in lockstep (one barrier per step); waves whose duo has
+    // fewer steps keep staging rows for the others.
+    // the chunk's block-table entries of each stream, copied once into LDS
+    // (read back per step with no long-lived registers): entry i of stream s
+    // is the page of index pa[s] + i
+    int* plist = (int*)(lds + LDS_SLICES + LDS_RING) + wave * 2 * PGMAX;
+    int pa[2], pcnt[2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      pa[s] = min(p0, last[s]) >> p.log2P;
+      pcnt[s] = min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX);
+      for (int i = lane; i < pcnt[s]; i += 64) plist[s * PGMAX + i] = len[s] > 0 ? btb[s][pa[s] + i] : 0;
+    }
+    if (lane == 0) wsteps[wave] = my_steps;
+    __syncthreads();
+    int nst = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) nst = max(nst, wsteps[w]);
+    nst = (nst + 5) / 6 * 6;                 // six steps per iteration (ring x row buffers)
+    constexpr int PIECES = TSTEP / 16 / WAVES;   // 16-byte pieces per wave and step
+    const int glast_st = (max(p.max_seq_len - 1, 0) >> 4) << 4;
+    float4v sb[2];                           // staged pieces in flight
+    auto stage_load = [&](int st, float4v& dst) {
+      const int gt = min(p0 + st * NT, glast_st);
+      if (lane < PIECES) dst = ((const float4v*)p.rope)[(size_t)(gt >> 2) * FP * 16 + wave * PIECES + lane];
+    };
+    auto stage_store = [&](int st, const float4v& v) {
+      if (lane < PIECES) *(float4v*)(lds + LDS_SLICES + (st & 1) * TSTEP + (wave * PIECES + lane) * 16) = v;
+    };
+    auto table_lds = [&](int st) {
+      const uint8_t* ring = lds + LDS_SLICES + (st & 1) * TSTEP + tbo;
+#pragma unroll
+      for (int j = 0; j < FP; ++j) tb[j] = *(const float4v*)(ring + j * 256);
+    };
+    // this wave's LDS writes are done, then the workgroup meets
+    auto wg_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0), other counters untouched
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ __volatile__("" ::: "memory");
+    };
+    // page ids of step st (uniform values, clamped into the chunk's list)
+    auto page_lds = [&](int st, int* pg) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        pg[s] = plist[s * PGMAX + min((min(p0 + st * NT, last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
+    };
+    uint32_t kw[3][NS][LW], vw[3][2][LW];
+    // one step: the rows of st+3 go to row buffer b3 = st % 3; staged pieces
+    // alternate with b2 = st % 2
+    // (scheduling fences keep the phases in this order, which bounds the
+    // live registers: the compiler would otherwise hoist loads and spill)
+    auto st_step = [&](int st, int b3, int b2) {
+      wg_barrier();                                   // ring slot st&1 holds the rows of st
+      stage_load(st + 2, sb[b2]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < my_steps) {
+        float sc[2], sv2[2];
+        int pg[NS];
+        page_lds(st + 3, pg);
+        table_lds(st);
+        k_side(sc);
+        __builtin_amdgcn_sched_barrier(0);
+        gather_v(vw[b3]);                             // V entries of step st
+        row_load(st + 3, pg, kw[b3], vw[b3]);
+        __builtin_amdgcn_sched_barrier(0);
+        to_v_role(sc, sv2);
+        gather_k(kw[(b3 + 1) % 3]);                   // K entries of step st+1
+        __builtin_amdgcn_sched_barrier(0);
+        v_side(p0 + st * NT, sv2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stage_store(st + 1, sb[1 - b2]);
+    };
+    if (nst > 0) {
+      stage_load(0, sb[0]);
+      stage_load(1, sb[1]);
+      if (my_steps > 0) {
+        int pg[NS];
+        page_lds(0, pg);
+        row_load(0, pg, kw[0], vw[0]);
+        page_lds(1, pg);
+        row_load(1, pg, kw[1], vw[1]);
+        page_lds(2, pg);
+        row_load(2, pg, kw[2], vw[2]);
+        gather_k(kw[0]);
+      }
+      stage_store(0, sb[0]);
+      for (int st = 0; st < nst; st += 6) {
+        st_step(st, 0, 0);
+        st_step(st + 1, 1, 1);
+        st_step(st + 2, 2, 0);
+        st_step(st + 3, 0, 1);
+        st_step(st + 4, 1, 0);
+        st_step(st + 5, 2, 1);
+      }
+    }
+  }
+
+  // ---- merge the 8 position slots of each (pair, quarter) and write the
+  //      chunk's partials
+  __syncthreads();                       // every wave is done with the slices
+  float* red = (float*)lds + (size_t)wave * 64 * SW;
+  {
+    float* r = red + lane * SW;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      r[4 * u] = acc[u].x; r[4 * u + 1] = acc[u].y; r[4 * u + 2] = acc[u].z; r[4 * u + 3] = acc[u].w;
+    }
+    r[4 * U] = m;
+    r[4 * U + 1] = l;
+    r[4 * U + 2] = lx;
+  }
+  __syncthreads();
+  // one lane per (pair, quarter): row 2*sv, position slot la == 0
+  if (active && okq[sv] && rp == 0 && la == 0 && p0 < len[sv]) {
+    float M = -INFINITY;
+    for (int i = 0; i < 8; ++i) {
+      const float* r = red + ((2 * sv + (i >> 2)) * 16 + (i & 3) * 4 + lb) * SW;
+      if (r[4 * U + 1] > 0.f) M = fmaxf(M, r[4 * U]);
+    }
+    float4v o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) o[u] = (float4v){0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, LX = 0.f;
+    for (int i = 0; i < 8; ++i) {
+      const float* r = red + ((2 * sv + (i >> 2)) * 16 + (i & 3) * 4 + lb) * SW;
+      if (!(r[4 * U + 1] > 0.f)) continue;
+      const float wt = __builtin_amdgcn_exp2f(r[4 * U] - M);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int lc = 4 * u;
-        const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
-        *(float4v*)(op + base) = o[u] * inv;
+        o[u].x = fmaf(wt, r[4 * u], o[u].x);
+        o[u].y = fmaf(wt, r[4 * u + 1], o[u].y);
+        o[u].z = fmaf(wt, r[4 * u + 2], o[u].z);
+        o[u].w = fmaf(wt, r[4 * u + 3], o[u].w);
       }
-      if (lb == 0) p.part_lse[part] = L > 0.f ? M + log2f(LX) : -INFINITY;
+      L = fmaf(wt, r[4 * U + 1], L);
+      LX = fmaf(wt, r[4 * U + 2], LX);
     }
-    __syncthreads();
+    const size_t part = (size_t)(h * p.n_pairs + kq[sv]) * p.n_chunks + ch;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float* op = p.part_o + part * D;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int lc = 4 * u;
+      const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
+      *(float4v*)(op + base) = o[u] * inv;
+    }
+    if (lb == 0) p.part_lse[part] = L > 0.f ? M + log2f(LX) : -INFINITY;
   }
 }
 
@@ -520,9 +675,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p) {
 // ---------------------------------------------------------------- dispatch
 template <int D, int C, int BITS, bool QF32, bool SHARE>
 static void launch_split_sp(const DecodeParams& p, int grid, hipStream_t s) {
-  // a step's 16 positions lie in one page when pages hold at least 16 positions
-  if (p.log2P >= 4) hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true>), dim3(grid), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false>), dim3(grid), dim3(256), 0, s, p);
+  // a step's 16 positions lie in one page when pages hold at least 16
+  // positions; workgroup-shared RoPE rows need eight duos per head
+  if (p.log2P < 4) {
+    hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false, false>), dim3(grid), dim3(512), 0, s, p);
+    return;
+  }
+  if constexpr (!QF32) {
+    if (p.shared_rope) {
+      hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, SHARE, true, true>), dim3(grid), dim3(512), 0, s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true, false>), dim3(grid), dim3(512), 0, s, p);
 }
 
 template <int D, int C, int BITS>
