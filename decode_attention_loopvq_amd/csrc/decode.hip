@@ -1,7 +1,8 @@
 // Quantised split-K decode attention for LoopVQ on gfx950.
 //
 // What it computes [LoopVQ paper, hub.valency.io/works/W_7srt5hed_v1,
-// section 4 "System implementation", attention; App. C]: at loop step t every
+// section "System implementation", attention; appendix
+// "Optimizing pre-RoPE vector quantization serving efficiency"]: at loop step t every
 // cached token j of a request contributes its key rebuilt from the step's
 // codebook slice, rotated by RoPE at position j, and its value rebuilt the
 // same way; tokens are cut into splits whose partial softmax outputs are
@@ -9,31 +10,31 @@
 // softmax over all tokens.
 //
 // MI355X mapping (this file's own design, not the pages'):
-//  * A wave is 16 "lane blocks" of 4 lanes.  A block is one (request, query
-//    head) pair at one position; its 4 lanes each own a quarter of the RoPE
-//    frequencies, i.e. D/8 channel pairs {f, f + D/2}.  Blocks of one wave are
-//    NP pairs x NT positions (NP*NT = 16), so NP pairs at the same position
-//    read the same RoPE-table row (the pages' "several requests per block"
-//    table sharing, taken to 16 pairs).
-//  * The two index rows of a token are streamed with one load per lane: the
-//    cache row order puts the groups a lane needs side by side.
-//  * The K and V slices of the workgroup's KV head are staged once in LDS,
-//    replicated so that lane l always reads its own bank window: entry e for
-//    lane slot s lives at e*256 + kv*128 + s*entry_bytes, so random gathers of
-//    one wave hit disjoint banks.  Gather addresses come from one v_perm_b32.
-//  * Scores are exact: fp16 codebook channels and fp16 query pairs feed
-//    v_dot2_f32_f16 (products exact in fp32), and the fp32 cos/sin weights are
-//    applied with fp32 FMAs:  s = sum_f cos_f*X_f + sin_f*Y_f with
-//    X_f = q_f k_f + q_{f+D/2} k_{f+D/2} and Y_f = q_{f+D/2} k_f - q_f k_{f+D/2},
-//    which equals q . RoPE(k) (rotate-half RoPE).
-//  * The value side runs on the matrix cores: v_mfma_f32_4x4x4_16b_f16 with A
-//    = p*I (each block is one token, lane i supplies row i) and B = the lane's
-//    gathered V entries accumulates p*v in fp32 registers with no VALU work
-//    per channel.  p is rounded to fp16 for the product; the running sum l
-//    adds the same rounded p, so the output stays an exact convex combination.
-//  * Online softmax in the log2 domain with a lazy maximum: the running max m
-//    is only raised when a score exceeds it by more than 8 (so p <= 256), which
-//    makes rescaling rare.
+//  * A workgroup is eight waves on one KV head.  The head's K and V slices are
+//    staged once in LDS, every entry replicated over a 256-byte row (one copy
+//    per bank window), and lane l reads window l mod (256 / entry bytes):
+//    random code gathers of a wave then hit each of the 64 banks once per
+//    pass.  A gather address is one v_perm_b32 (code -> byte 1, lane window
+//    -> byte 0, K|V region -> byte 2).
+//  * A wave serves a duo of (request, query head) pairs 2i and 2i+1 over a
+//    chunk of positions, 16 positions per step.  When the GQA group is even
+//    the duo's pairs are query heads of one request and share one index
+//    stream and its key gathers.
+//  * K side: a lane owns one position (of its 16-lane row) and one quarter
+//    of the RoPE frequencies.  For each frequency one v_mfma_f32_4x4x4f16 with
+//    the block-diagonal query matrix [[q0_f, q0_h], [q0_h, -q0_f]] (+) the same
+//    for pair 1 and the key column (k0_f, k0_h, k1_f, k1_h) yields
+//    X = q_f k_f + q_h k_h and Y = q_h k_f - q_f k_h of both pairs with exact
+//    fp16 products; the lane then adds cos*X + sin*Y in fp32, which equals
+//    q . RoPE(k).  One load of cos/sin serves both pairs.
+//  * V side: rows 0-1 of the wave serve pair 0, rows 2-3 pair 1; a lane takes
+//    two positions and one channel quarter, and the same MFMA with A = p*I
+//    and the gathered V entries as B accumulates p*v in fp32 registers.
+//  * Online softmax in the log2 domain with a lazy maximum: the running max
+//    is only raised when a score exceeds it by more than 8 (so p <= 256).
+//  * RoPE rows come from a table interleaved by groups of 4 positions (one
+//    contiguous 256-byte run per 16 lanes); with eight duos per head the
+//    workgroup stages each step's rows once into an LDS ring (see below).
 #include <math.h>
 
 #include "common.h"

@@ -1,7 +1,8 @@
 // LoopVQ encoder on gfx950: nearest codebook entry of every coupled vector.
 //
 // What it computes [LoopVQ paper, hub.valency.io/works/W_7srt5hed_v1,
-// section 4.1 eq. 4 and section 2 eq. 2; section 4 "System implementation",
+// section "Loop-axis vector quantization", eq. (4), and section
+// "Preliminaries", eq. (2); section "System implementation",
 // encoding]: for token j, KV head h, x in {K, V}, block beta and group g the
 // coupled vector z[i*Tc + m] = x^(beta*Tc+m+1)[j][h][g*c + i] is replaced by
 // argmin_r ||z - e_r||^2 (lowest r on ties), written into the paged index row.

@@ -6,11 +6,12 @@
  * hub.valency.io/works/W_7srt5hed_v1) quantises the KV cache of a looped
  * transformer along the loop axis: T loop steps are cut into blocks of Tc
  * consecutive steps, and one b-bit code covers c channels at each of the Tc
- * steps of a block (a coupled vector of G = c*Tc elements, section 4.1,
- * eq. 4).  Loop step beta*Tc + m + 1 reads the shared code through its own
- * slice of the codebook entry, coordinates i*Tc + m for i < c (eq. 5 and
- * section 4 "System implementation").  Keys are coded before RoPE, and the
- * decode kernel applies RoPE to every rebuilt key (section 2, App. C).
+ * steps of a block (a coupled vector of G = c*Tc elements, section "Loop-axis vector
+ * quantization", eq. (4)).  Loop step beta*Tc + m + 1 reads the shared code through its own
+ * slice of the codebook entry, coordinates i*Tc + m for i < c (eq. (5) and
+ * section "System implementation").  Keys are coded before RoPE, and the
+ * decode kernel applies RoPE to every rebuilt key (section "Preliminaries"; appendix "Optimizing pre-RoPE vector
+ * quantization serving efficiency").
  *
  * Conventions
  *   - Every pointer is a device pointer unless marked [host].  The caller owns
@@ -94,7 +95,7 @@ int loopvq_row_bytes(const loopvq_dims* dims);
 /*
  * Cut the per-loop-step codebook slices once at load time, and compute
  * hsq = 0.5*||e||^2 of every entry (in fp64, rounded to fp32) for the encoder.
- * [LoopVQ paper, section 4 "System implementation": the slice B_t holds
+ * [LoopVQ paper, section "System implementation": the slice B_t holds
  * coordinate i*Tc + m of every entry, cut once when the model is loaded.]
  *   n_blocks = T / Tc codebooks per (KV head, K|V).
  *   cb      [n_blocks][H_kv][2][K][G] fp16 (input)
@@ -128,7 +129,7 @@ size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D);
  * the coupled vector z[i*Tc + m] = x^(beta*Tc+m+1)[j][h][g*c + i] (eq. 4)
  * is replaced by the index of its nearest codebook entry in squared L2
  * distance, ties to the lowest index (eq. 2), and written to slot g's place
- * in the row of token j.  [LoopVQ paper, section 4 "System implementation",
+ * in the row of token j.  [LoopVQ paper, section "System implementation",
  * encoding: distances to all entries as a matrix product, then the nearest
  * entry.]
  *   n_tok         tokens in this call (n_tok >= 0; 0 is a no-op).
@@ -159,10 +160,10 @@ size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
 
 /*
  * Quantised decode attention of B requests at loop step t (1-based).
- * [LoopVQ paper, section 4 "System implementation", attention: at loop step
+ * [LoopVQ paper, section "System implementation", attention: at loop step
  * t the kernel looks up each index in B_t, rebuilds K, applies RoPE, and
  * splits the tokens across workgroups whose partial outputs are merged by
- * their logsumexp, which recovers the exact softmax; App. C.]
+ * their logsumexp, which recovers the exact softmax.]
  *   t             loop step, 1 <= t <= T; reads block (t-1)/Tc, slice t-1.
  *   q             [B][H_q][D] queries already rotated at their own position.
  *   index_cache   the cache of block (t-1)/Tc.
@@ -198,7 +199,7 @@ int loopvq_decode_attn(const loopvq_dims* dims, int32_t t, int32_t B,
  * loopvq_decode_combine merges them into out and lse.  Both must be given the
  * same dims, B, seq_lens, max_seq_len and workspace, on the same stream (or
  * with the caller ordering them).  Arguments mean what they mean for
- * loopvq_decode_attn.  [LoopVQ paper, section 4 "System implementation":
+ * loopvq_decode_attn.  [LoopVQ paper, section "System implementation":
  * split partial outputs combined through the logsumexp of their scores.]
  */
 int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,

@@ -15,12 +15,12 @@ module rebuilds one from the prose it says which sentence it follows.
 
 Readings taken where the pages are silent (each also listed in the design doc):
   * channel group g covers the contiguous channels [g*c, (g+1)*c) at every loop
-    step of the block (P1 section 2 "Vector quantization of the KV cache": G
+    step of the block (P1 section "Preliminaries", "Vector quantization of the KV cache": G
     contiguous channels; no permutation outside TaSQ);
   * one codebook per (layer, KV head, K|V, block), shared by all groups g;
   * indices are stored 0-based (entry e_{r+1} is code r);
   * ties in the nearest-entry rule go to the lowest index;
-  * RoPE uses the rotate-half pairs {f, f + D/2} (P1 App. B "Grouping under
+  * RoPE uses the rotate-half pairs {f, f + D/2} (P1 appendix "Grouping under
     loop coupling" keeps RoPE pairs {i, i + D/2} together) with
     theta_f = base^(-2f/D) and position = the token's 0-based index;
   * the decode query arrives already rotated at its own position, and the
@@ -42,7 +42,7 @@ NEAR_TIE_REL = 1e-6
 
 
 # --------------------------------------------------------------------------
-# coupled vectors  [P1 section 4.1 "Loop-axis vector quantization", eq. (4);
+# coupled vectors  [P1 section "Loop-axis vector quantization", eq. (4);
 #                   P2 section 3.1: coordinate i*Tc + m of the coupled vector]
 # --------------------------------------------------------------------------
 def coupled_vectors(x: np.ndarray, Tc: int, c: int, beta: int) -> np.ndarray:
@@ -69,7 +69,7 @@ def coupled_vectors(x: np.ndarray, Tc: int, c: int, beta: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# nearest-entry encoding  [P1 section 2, eq. (2); P2 "Terms to know first":
+# nearest-entry encoding  [P1 section "Preliminaries", eq. (2); P2 "Terms to know first":
 #                          a(z) = argmin_r ||z - e_r||^2]
 # --------------------------------------------------------------------------
 @dataclass
@@ -162,7 +162,7 @@ def encode_stream(x: np.ndarray, E: np.ndarray, Tc: int, c: int, beta: int,
 
 
 # --------------------------------------------------------------------------
-# index rows  [P1 section 4 "System implementation", cache layout: a quantised
+# index rows  [P1 section "System implementation", cache layout: a quantised
 #              page stores one index row per block; b bits per code]
 # --------------------------------------------------------------------------
 def row_group_order(n_groups: int) -> np.ndarray:
@@ -240,7 +240,7 @@ def gather_rows(cache: np.ndarray, block_table_row: np.ndarray, n: int, h: int, 
 
 
 # --------------------------------------------------------------------------
-# loop slices and reconstruction  [P1 section 4.1, eq. (5); section 4
+# loop slices and reconstruction  [P1 section "Loop-axis vector quantization", eq. (5); section
 #   "System implementation": loop step beta*Tc + m + 1 reads coordinates
 #   [e]_{i*Tc + m}, i < c, of the chosen entry]
 # --------------------------------------------------------------------------
@@ -259,7 +259,8 @@ def rebuild(idx: np.ndarray, E: np.ndarray, Tc: int, c: int, m: int) -> np.ndarr
 
 
 # --------------------------------------------------------------------------
-# RoPE  [P1 section 2 and App. C: keys are quantised before RoPE, which the
+# RoPE  [P1 section "Preliminaries" and appendix "Optimizing pre-RoPE vector
+#        quantization serving efficiency": keys are quantised before RoPE, which the
 #        attention applies to the reconstructed key at the token's position]
 # --------------------------------------------------------------------------
 def rope_frequencies(D: int, base: float) -> np.ndarray:
@@ -288,7 +289,7 @@ def rope_table(max_pos: int, D: int, base: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# attention  [P1 section 4 "System implementation": the split partials are
+# attention  [P1 section "System implementation": the split partials are
 #   merged by their logsumexp, which recovers the exact softmax over all
 #   tokens - so the reference is plain dense softmax attention]
 # --------------------------------------------------------------------------
@@ -366,5 +367,5 @@ def build_index_cache(xk: np.ndarray, xv: np.ndarray, cb: np.ndarray, Tc: int, c
 
 
 def bits_per_element(bits: int, G: int) -> float:
-    """Storage cost of one code of b bits covering G elements [P1 section 2]."""
+    """Storage cost of one code of b bits covering G elements [P1 section "Preliminaries"]."""
     return bits / G
