@@ -55,7 +55,7 @@ __device__ __forceinline__ void load_run(const void* base, size_t off, float* v)
   }
 }
 
-template <int G, bool XF32, int BITS>
+template <int G, int C, bool XF32, int BITS>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   constexpr int KD = XF32 ? 2 * G : G;          // reduction length with the fp32 split
   constexpr int KDP = KD < 16 ? 16 : KD;        // padded to the MFMA depth
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int kc = lane >> 4, col = lane & 15;
 
   // ---- entry operands (rows = entries) and -0.5||e||^2 accumulator inputs
@@ -104,104 +104,160 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   }
 
   const int n = D / c;                 // groups per token
+  const int UPT = n / 16;              // work units (16 groups each) per token (1, 2 or 4)
+  const int LUPT = __builtin_ctz(UPT);
   const int R = n * BITS / 8;
   const int P = 1 << p.log2P;
   const void* xsrc = kv ? p.xv : p.xk;
-  constexpr int CHMAX = KSTEP;
-  const int tok0 = (blockIdx.x * 4 + wave) * p.tok_per_wave;
-  const int tok1 = min(tok0 + p.tok_per_wave, p.n_tok);
+  constexpr int CH = KSTEP < C ? KSTEP : C;   // elements per contiguous run
+  const int u0 = (blockIdx.x * 4 + wave) * p.tok_per_wave * UPT;
+  const int u1 = min(u0 + p.tok_per_wave * UPT, p.n_tok * UPT);
+  if (u0 >= u1) return;                // no work (no barrier follows)
 
-  for (int tok = tok0; tok < tok1; ++tok) {
-    const int slot = p.slot_mapping[tok];
-    uint8_t* row = p.cache + (int64_t)beta * p.block_stride +
-                   ((((size_t)(slot >> p.log2P) * H + h) * 2 + kv) * P + (slot & (P - 1))) * R;
-    for (int g0 = 0; g0 < n; g0 += 16) {
-      const int g = g0 + col;
-      // ---- vector operand (columns = vectors)
-      OpT Bv[NMF];
+  // raw operand elements of one unit, loaded as fp32 (exact for bf16 and fp32)
+  // KSTEP elements per lane and MFMA: runs of `ch` contiguous channels of one
+  // loop step; elements past the reduction length KD are zero
+  struct Raw { float v[NMF][KSTEP]; };
+  // element offset of run (mu, jc) of this lane: a lane-constant part (loop
+  // step, channel) plus a wave-uniform part (token, head, group batch)
+  const size_t step_stride = (size_t)p.n_tok * H * D;
+  size_t lane_off[NMF][KSTEP / CH];
+  bool run_ok[NMF][KSTEP / CH];
 #pragma unroll
-      for (int mu = 0; mu < NMF; ++mu) {
-        const int k0 = mu * MF + kc * KSTEP;
-        // runs of CH contiguous channels of one loop step
-        const int CH = KSTEP < c ? KSTEP : c;
+  for (int mu = 0; mu < NMF; ++mu)
 #pragma unroll
-        for (int j = 0; j < KSTEP; ++j) Bv[mu][j] = (_Float16)0.f;
-        for (int jc = 0; jc < KSTEP; jc += CH) {
-          const int kap = k0 + jc;
-          if (kap >= KD) break;
-          const bool lo_part = XF32 && kap >= G;
-          const int kp = lo_part ? kap - G : kap;
-          const int m = kp / c, i0 = kp - m * c;
-          const size_t off = (((size_t)(beta * Tc + m) * p.n_tok + tok) * H + h) * D + g * c + i0;
-          float v[CHMAX];
-          if (CH == KSTEP) load_run<XF32, KSTEP>(xsrc, off, v);
-          else {
+    for (int q = 0; q < KSTEP / CH; ++q) {
+      const int kap = mu * MF + kc * KSTEP + q * CH;
+      run_ok[mu][q] = kap < KD;
+      const int kp = (XF32 && kap >= G) ? kap - G : kap;
+      const int m = kp / C, i0 = kp - m * C;
+      lane_off[mu][q] = (size_t)(beta * Tc + m) * step_stride + (size_t)col * C + i0;
+    }
+  // row slot of group g (the row order of the cache; q = n/8 is a power of two)
+  const int lq = __builtin_ctz(n >> 3), hgr = n >> 1;
+  auto slot_of = [&](int g) {
+    const bool hi = g >= hgr;
+    const int gg = hi ? g - hgr : g;
+    return ((gg >> lq) << (lq + 1)) + (hi ? (1 << lq) : 0) + (gg & ((1 << lq) - 1));
+  };
+  auto load_raw = [&](int u, Raw& r) {
+    const int uu = min(u, u1 - 1);                 // clamped: loads stay in bounds
+    const int tok = uu >> LUPT, gb = uu & (UPT - 1);
+    const size_t uoff = ((size_t)tok * H + h) * D + (size_t)gb * 16 * C;
 #pragma unroll
-            for (int j = 0; j < CHMAX; ++j) v[j] = 0.f;
-            for (int j = 0; j < CH; ++j) {
-              float tmp[1];
-              load_run<XF32, 1>(xsrc, off + j, tmp);
-              v[j] = tmp[0];
-            }
-          }
-          for (int j = 0; j < CH; ++j) {
-            const _Float16 hi = (_Float16)v[j];
-            Bv[mu][jc + j] = lo_part ? (_Float16)(v[j] - (float)hi) : hi;
-          }
-        }
+    for (int mu = 0; mu < NMF; ++mu)
+#pragma unroll
+      for (int q = 0; q < KSTEP / CH; ++q) {
+        float v[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) v[j] = 0.f;
+        if (run_ok[mu][q]) load_run<XF32, CH>(xsrc, uoff + lane_off[mu][q], v);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) r.v[mu][q * CH + j] = v[j];
       }
-      // ---- scores against all entries, running argmax
-      float best = -INFINITY;
-      int bidx = 0;
+  };
+  // fp16 operand: bf16 values convert exactly; fp32 values are split into a
+  // high part (reduction index < G) and a low part (index >= G)
+  auto to_operand = [&](const Raw& r, OpT* Bv) {
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) {
-        float4v d = Cin[t];
+    for (int mu = 0; mu < NMF; ++mu) {
 #pragma unroll
-        for (int mu = 0; mu < NMF; ++mu) {
-          if constexpr (MF == 32) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t][mu], Bv[mu], d, 0, 0, 0);
-          else d = __builtin_amdgcn_mfma_f32_16x16x16f16(A[t][mu], Bv[mu], d, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool better = d[r] > best;
-          best = better ? d[r] : best;
-          bidx = better ? 16 * t + 4 * kc + r : bidx;
-        }
-      }
-      // ---- merge the four lanes holding the same vector
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bidx, off);
-        const bool take = ob > best || (ob == best && oi < bidx);
-        best = take ? ob : best;
-        bidx = take ? oi : bidx;
-      }
-      // ---- write the code into its row slot
-      const int s = row_slot_of_group(g, n);
-      if constexpr (BITS == 8) {
-        if (kc == 0) row[s] = (uint8_t)bidx;
-      } else {
-        const int other = __shfl_xor(bidx, 1);
-        if (kc == 0 && (col & 1) == 0) row[s >> 1] = (uint8_t)((bidx & 15) | ((other & 15) << 4));
+      for (int j = 0; j < KSTEP; ++j) {
+        const int kap = mu * MF + kc * KSTEP + j;
+        const float v = r.v[mu][j];
+        const _Float16 hi = (_Float16)v;
+        Bv[mu][j] = (XF32 && kap >= G && kap < KD) ? (_Float16)(v - (float)hi) : hi;
       }
     }
+  };
+
+  // software pipeline over units: the raw loads of unit u+3 are issued while
+  // unit u is scored
+  Raw rb[4];
+  load_raw(u0, rb[0]);
+  load_raw(u0 + 1, rb[1]);
+  load_raw(u0 + 2, rb[2]);
+  auto do_unit = [&](int u, Raw& cur, Raw& nxt) {
+    OpT Bv[NMF];
+    to_operand(cur, Bv);
+    load_raw(u + 3, nxt);
+    const int tok = u >> LUPT, gb = u & (UPT - 1);
+    const int slot = p.slot_mapping[tok];
+    // ---- scores against all entries: per 16-entry tile the lane sees 4
+    //      entries (rows 4*kc .. 4*kc+3) of its vector.  It keeps the best
+    //      tile (strict compare in increasing tile order) and that tile's four
+    //      scores; the lowest row holding the maximum is resolved at the end,
+    //      so the whole search takes the lowest index on exact ties.
+    float best = -INFINITY, bd0 = 0.f, bd1 = 0.f, bd2 = 0.f, bd3 = 0.f;
+    int btile = 0;
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      float4v d = Cin[t];
+#pragma unroll
+      for (int mu = 0; mu < NMF; ++mu) {
+        if constexpr (MF == 32) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t][mu], Bv[mu], d, 0, 0, 0);
+        else d = __builtin_amdgcn_mfma_f32_16x16x16f16(A[t][mu], Bv[mu], d, 0, 0, 0);
+      }
+      float m3 = __builtin_fmaxf(__builtin_fmaxf(d.x, d.y), d.z);
+      m3 = __builtin_fmaxf(m3, d.w);
+      const bool better = m3 > best;
+      best = better ? m3 : best;
+      btile = better ? t : btile;
+      bd0 = better ? d.x : bd0;
+      bd1 = better ? d.y : bd1;
+      bd2 = better ? d.z : bd2;
+      bd3 = better ? d.w : bd3;
+    }
+    const int r = bd0 == best ? 0 : (bd1 == best ? 1 : (bd2 == best ? 2 : 3));
+    int bidx = 16 * btile + 4 * kc + r;
+    // ---- merge the four lanes holding the same vector (lower index on ties)
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bidx, off);
+      const bool take = ob > best || (ob == best && oi < bidx);
+      best = take ? ob : best;
+      bidx = take ? oi : bidx;
+    }
+    // ---- write the code into its row slot
+    uint8_t* row = p.cache + (int64_t)beta * p.block_stride +
+                   ((((size_t)(slot >> p.log2P) * H + h) * 2 + kv) * P + (slot & (P - 1))) * R;
+    const int sl = slot_of(gb * 16 + col);
+    if constexpr (BITS == 8) {
+      if (kc == 0) row[sl] = (uint8_t)bidx;
+    } else {
+      const int other = __shfl_xor(bidx, 1);
+      if (kc == 0 && (col & 1) == 0) row[sl >> 1] = (uint8_t)((bidx & 15) | ((other & 15) << 4));
+    }
+  };
+  int u = u0;
+  for (; u + 4 <= u1; u += 4) {
+    do_unit(u, rb[0], rb[3]);
+    do_unit(u + 1, rb[1], rb[0]);
+    do_unit(u + 2, rb[2], rb[1]);
+    do_unit(u + 3, rb[3], rb[2]);
   }
+  if (u < u1) do_unit(u, rb[0], rb[3]);
+  if (u + 1 < u1) do_unit(u + 1, rb[1], rb[0]);
+  if (u + 2 < u1) do_unit(u + 2, rb[2], rb[1]);
 }
 
-template <int G, bool XF32, int BITS>
+template <int G, int C, bool XF32, int BITS>
 static hipError_t launch_encode_t(const EncodeParams& p, int n_blocks, hipStream_t s) {
   dim3 grid(p.n_tok_groups, n_blocks * 2 * p.H_kv);
-  hipLaunchKernelGGL((encode_kernel<G, XF32, BITS>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s) {
-#define LVQ_ENC(g, f, b) if (G == g && xf32 == f && bits == b) return launch_encode_t<g, f, b>(p, n_blocks, s);
-  LVQ_ENC(16, false, 8) LVQ_ENC(32, false, 8) LVQ_ENC(8, false, 8)
-  LVQ_ENC(16, true, 8) LVQ_ENC(8, true, 8) LVQ_ENC(32, true, 8)
-  LVQ_ENC(16, false, 4) LVQ_ENC(32, false, 4) LVQ_ENC(8, false, 4)
-  LVQ_ENC(16, true, 4) LVQ_ENC(8, true, 4) LVQ_ENC(32, true, 4)
+  const int c = p.c;
+#define LVQ_ENC(g, cc, f, b) \
+  if (G == g && c == cc && xf32 == f && bits == b) return launch_encode_t<g, cc, f, b>(p, n_blocks, s);
+#define LVQ_ENC_C(g, f, b) LVQ_ENC(g, 2, f, b) LVQ_ENC(g, 4, f, b) LVQ_ENC(g, 8, f, b)
+  LVQ_ENC_C(16, false, 8) LVQ_ENC_C(32, false, 8) LVQ_ENC_C(16, false, 4) LVQ_ENC_C(32, false, 4)
+  LVQ_ENC_C(8, true, 8) LVQ_ENC_C(16, true, 8) LVQ_ENC_C(32, true, 8)
+  LVQ_ENC_C(8, true, 4) LVQ_ENC_C(16, true, 4) LVQ_ENC_C(32, true, 4)
+#undef LVQ_ENC_C
 #undef LVQ_ENC
   return hipErrorInvalidValue;
 }
