@@ -170,11 +170,13 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, i
   p.Tc = dims->Tc;
   p.K = K;
   p.log2P = ilog2(dims->page_size);
+  // units of 32 (token, group) vectors; about 8192 waves over the whole call
   const long long streams = (long long)n_blocks * 2 * H;
-  long long tpw = (streams * n_tok + 4LL * 2048 - 1) / (4LL * 2048);
-  tpw = std::max<long long>(1, std::min<long long>(tpw, n_tok));
-  p.tok_per_wave = (int)tpw;
-  p.n_tok_groups = (int)((n_tok + 4 * tpw - 1) / (4 * tpw));
+  const long long units = ((long long)n_tok * (dims->D / dims->c) + 31) / 32;
+  long long upw = (streams * units + 8191) / 8192;
+  upw = std::max<long long>(1, std::min<long long>(upw, units));
+  p.units_per_wave = (int)upw;
+  p.n_unit_groups = (int)((units + 4 * upw - 1) / (4 * upw));
   return hip_status(launch_encode(G, dims->x_dtype == LOOPVQ_DTYPE_F32, dims->bits, p, n_blocks, stream));
 }
 

@@ -29,146 +29,148 @@
 
 namespace loopvq {
 
-template <bool XF32, int CH>
-__device__ __forceinline__ void load_run(const void* base, size_t off, float* v) {
-  if constexpr (XF32) {
-    const float* s = (const float*)base + off;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) v[j] = s[j];
-  } else {
-    const uint16_t* s = (const uint16_t*)base + off;
-    if constexpr (CH == 8) {
-      uint4v w = *(const uint4v*)s;
-      uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { v[2 * j] = bf16lo(ww[j]); v[2 * j + 1] = bf16hi(ww[j]); }
-    } else if constexpr (CH == 4) {
-      uint2v w = *(const uint2v*)s;
-      v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
-    } else if constexpr (CH == 2) {
-      uint32_t w = *(const uint32_t*)s;
-      v[0] = bf16lo(w); v[1] = bf16hi(w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) v[j] = u2f((uint32_t)s[j] << 16);
-    }
-  }
-}
-
 template <int G, int C, bool XF32, int BITS>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
-  constexpr int KD = XF32 ? 2 * G : G;          // reduction length with the fp32 split
+  constexpr int KD = XF32 ? 2 * G : G;          // reduction length (fp32: high and low halves)
   constexpr int KDP = KD < 16 ? 16 : KD;        // padded to the MFMA depth
-  constexpr int MF = (KDP % 32 == 0) ? 32 : 16; // 16x16x32 or 16x16x16
-  constexpr int KSTEP = MF / 4;                 // operand elements per lane per MFMA
-  constexpr int NMF = KDP / MF;
+  constexpr int NMF = KDP / 16;                 // 32x32x16 MFMAs per tile
   constexpr int KENT = 1 << BITS;
-  constexpr int NTILE = KENT / 16;
-  using OpT = typename std::conditional<MF == 32, half8v, half4v>::type;
+  constexpr int NTILE = KENT >= 32 ? KENT / 32 : 1;   // 4-bit: one tile, rows 16..31 unused
+  constexpr int CH = C < 8 ? C : 8;             // channels per contiguous run of one loop step
+  constexpr int NRUN = 8 / CH;                  // runs per lane and MFMA
+  constexpr int RW = XF32 ? CH : CH / 2;        // 32-bit words per run
 
   __shared__ uint16_t cbp[KENT * G];
+  // -0.5*||e||^2 of the 16 rows a lane holds per tile, [t][h][16] (h = lane / 32;
+  // rows 8q + 4h + s), the MFMA accumulator inputs; -inf on unused rows
+  __shared__ __attribute__((aligned(16))) float hsl[NTILE * 2 * 16];
 
-  const int H = p.H_kv, c = p.c, Tc = p.Tc, D = p.D;
+  const int H = p.H_kv, Tc = p.Tc, D = p.D;
   const int y = blockIdx.y;
-  const int h = y % H, kv = (y / H) & 1, beta = y / (2 * H);
+  const int hd = y % H, kv = (y / H) & 1, beta = y / (2 * H);
 
-  // ---- codebook of (beta, h, kv), permuted to loop-major coordinates
-  const uint16_t* cbsrc = p.cb + ((size_t)(beta * H + h) * 2 + kv) * KENT * G;
+  // ---- codebook of (beta, hd, kv), permuted to loop-major coordinates
+  const uint16_t* cbsrc = p.cb + ((size_t)(beta * H + hd) * 2 + kv) * KENT * G;
   for (int x = threadIdx.x; x < KENT * G; x += blockDim.x) {
     const int e = x / G, kap = x - e * G;
-    const int m = kap / c, i = kap - m * c;
+    const int m = kap / C, i = kap - m * C;
     cbp[x] = cbsrc[(size_t)e * G + i * Tc + m];
+  }
+  for (int x = threadIdx.x; x < NTILE * 32; x += blockDim.x) {
+    const int t = x >> 5, hh = (x >> 4) & 1, q = (x >> 2) & 3, sr = x & 3;
+    const int e = 32 * t + 8 * q + 4 * hh + sr;
+    hsl[x] = e < KENT ? -p.hsq[((size_t)(beta * H + hd) * 2 + kv) * KENT + e] : -INFINITY;
   }
   __syncthreads();
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int kc = lane >> 4, col = lane & 15;
+  const int hf = lane >> 5, col = lane & 31;
 
-  // ---- entry operands (rows = entries) and -0.5||e||^2 accumulator inputs
-  OpT A[NTILE][NMF];
-  float4v Cin[NTILE];
-  const float* hs = p.hsq + ((size_t)(beta * H + h) * 2 + kv) * KENT;
+  // ---- entry operands (rows = entries 32t + col, reduction chunk hf), held
+  //      for the life of the wave
+  half8v A[NTILE][NMF];
 #pragma unroll
-  for (int t = 0; t < NTILE; ++t) {
+  for (int t = 0; t < NTILE; ++t)
 #pragma unroll
-    for (int mu = 0; mu < NMF; ++mu) {
+    for (int mu = 0; mu < NMF; ++mu)
 #pragma unroll
-      for (int j = 0; j < KSTEP; ++j) {
-        const int kap = mu * MF + kc * KSTEP + j;
-        const uint16_t bits = kap < KD ? cbp[(16 * t + col) * G + (kap % G)] : (uint16_t)0;
+      for (int j = 0; j < 8; ++j) {
+        const int kap = 16 * mu + 8 * hf + j;
+        const int e = 32 * t + col;
+        const uint16_t bits = (kap < KD && e < KENT) ? cbp[e * G + (kap % G)] : (uint16_t)0;
         A[t][mu][j] = __builtin_bit_cast(_Float16, bits);
       }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Cin[t][r] = -hs[16 * t + 4 * kc + r];
-  }
 
-  const int n = D / c;                 // groups per token
-  const int UPT = n / 16;              // work units (16 groups each) per token (1, 2 or 4)
-  const int LUPT = __builtin_ctz(UPT);
+  const int n = D / C;                 // groups (vectors) per token, a power of two
+  const int ln = __builtin_ctz(n);
   const int R = n * BITS / 8;
   const int P = 1 << p.log2P;
   const void* xsrc = kv ? p.xv : p.xk;
-  constexpr int CH = KSTEP < C ? KSTEP : C;   // elements per contiguous run
-  const int u0 = (blockIdx.x * 4 + wave) * p.tok_per_wave * UPT;
-  const int u1 = min(u0 + p.tok_per_wave * UPT, p.n_tok * UPT);
+  const int nvec = p.n_tok * n;        // vectors of this stream
+  const int nunit = (nvec + 31) >> 5;  // units of 32 vectors
+  const int u0 = (blockIdx.x * 4 + wave) * p.units_per_wave;
+  const int u1 = min(u0 + p.units_per_wave, nunit);
   if (u0 >= u1) return;                // no work (no barrier follows)
 
-  // raw operand elements of one unit, loaded as fp32 (exact for bf16 and fp32)
-  // KSTEP elements per lane and MFMA: runs of `ch` contiguous channels of one
-  // loop step; elements past the reduction length KD are zero
-  struct Raw { float v[NMF][KSTEP]; };
-  // element offset of run (mu, jc) of this lane: a lane-constant part (loop
-  // step, channel) plus a wave-uniform part (token, head, group batch)
+  // element offset of run (mu, q) of this lane, without the token/group part
   const size_t step_stride = (size_t)p.n_tok * H * D;
-  size_t lane_off[NMF][KSTEP / CH];
-  bool run_ok[NMF][KSTEP / CH];
+  size_t run_off[NMF][NRUN];
+  bool run_ok[NMF][NRUN];
 #pragma unroll
   for (int mu = 0; mu < NMF; ++mu)
 #pragma unroll
-    for (int q = 0; q < KSTEP / CH; ++q) {
-      const int kap = mu * MF + kc * KSTEP + q * CH;
+    for (int q = 0; q < NRUN; ++q) {
+      const int kap = 16 * mu + 8 * hf + q * CH;
       run_ok[mu][q] = kap < KD;
       const int kp = (XF32 && kap >= G) ? kap - G : kap;
       const int m = kp / C, i0 = kp - m * C;
-      lane_off[mu][q] = (size_t)(beta * Tc + m) * step_stride + (size_t)col * C + i0;
+      run_off[mu][q] = (size_t)(beta * Tc + m) * step_stride + (size_t)hd * D + i0;
     }
+  // raw input words of one unit (bf16 pairs or fp32), converted at use
+  struct Raw { uint32_t w[NMF][NRUN][RW]; };
+  auto load_raw = [&](int u, Raw& r) {
+    const int v = min(u * 32 + col, nvec - 1);     // clamped: loads stay in bounds
+    const int tok = v >> ln, g = v & (n - 1);
+    const size_t voff = (size_t)tok * H * D + (size_t)g * C;
+#pragma unroll
+    for (int mu = 0; mu < NMF; ++mu)
+#pragma unroll
+      for (int q = 0; q < NRUN; ++q) {
+#pragma unroll
+        for (int j = 0; j < RW; ++j) r.w[mu][q][j] = 0u;
+        if (!run_ok[mu][q]) continue;
+        const size_t off = voff + run_off[mu][q];
+        if constexpr (XF32) {
+          const float* s = (const float*)xsrc + off;
+          if constexpr (CH == 8) {
+            const float4v a = *(const float4v*)s, b = *(const float4v*)(s + 4);
+            r.w[mu][q][0] = f2u(a.x); r.w[mu][q][1] = f2u(a.y); r.w[mu][q][2] = f2u(a.z); r.w[mu][q][3] = f2u(a.w);
+            r.w[mu][q][4] = f2u(b.x); r.w[mu][q][5] = f2u(b.y); r.w[mu][q][6] = f2u(b.z); r.w[mu][q][7] = f2u(b.w);
+          } else if constexpr (CH == 4) {
+            const float4v a = *(const float4v*)s;
+            r.w[mu][q][0] = f2u(a.x); r.w[mu][q][1] = f2u(a.y); r.w[mu][q][2] = f2u(a.z); r.w[mu][q][3] = f2u(a.w);
+          } else {
+            const uint2v a = *(const uint2v*)s;
+            r.w[mu][q][0] = a.x; r.w[mu][q][1] = a.y;
+          }
+        } else {
+          const uint16_t* s = (const uint16_t*)xsrc + off;
+          if constexpr (CH == 8) {
+            const uint4v a = *(const uint4v*)s;
+            r.w[mu][q][0] = a.x; r.w[mu][q][1] = a.y; r.w[mu][q][2] = a.z; r.w[mu][q][3] = a.w;
+          } else if constexpr (CH == 4) {
+            const uint2v a = *(const uint2v*)s;
+            r.w[mu][q][0] = a.x; r.w[mu][q][1] = a.y;
+          } else {
+            r.w[mu][q][0] = *(const uint32_t*)s;
+          }
+        }
+      }
+  };
+  // fp16 operand: bf16 values convert exactly; fp32 values are split into a
+  // high part (reduction index < G) and a low part (index >= G)
+  auto to_operand = [&](const Raw& r, half8v* Bv) {
+#pragma unroll
+    for (int mu = 0; mu < NMF; ++mu)
+#pragma unroll
+      for (int q = 0; q < NRUN; ++q)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const int kap = 16 * mu + 8 * hf + q * CH + j;
+          float v;
+          if constexpr (XF32) v = u2f(r.w[mu][q][j]);
+          else v = (j & 1) ? bf16hi(r.w[mu][q][j >> 1]) : bf16lo(r.w[mu][q][j >> 1]);
+          const _Float16 hi = (_Float16)v;
+          Bv[mu][q * CH + j] = (XF32 && kap >= G && kap < KD) ? (_Float16)(v - (float)hi) : hi;
+        }
+  };
+
   // row slot of group g (the row order of the cache; q = n/8 is a power of two)
   const int lq = __builtin_ctz(n >> 3), hgr = n >> 1;
   auto slot_of = [&](int g) {
     const bool hi = g >= hgr;
     const int gg = hi ? g - hgr : g;
     return ((gg >> lq) << (lq + 1)) + (hi ? (1 << lq) : 0) + (gg & ((1 << lq) - 1));
-  };
-  auto load_raw = [&](int u, Raw& r) {
-    const int uu = min(u, u1 - 1);                 // clamped: loads stay in bounds
-    const int tok = uu >> LUPT, gb = uu & (UPT - 1);
-    const size_t uoff = ((size_t)tok * H + h) * D + (size_t)gb * 16 * C;
-#pragma unroll
-    for (int mu = 0; mu < NMF; ++mu)
-#pragma unroll
-      for (int q = 0; q < KSTEP / CH; ++q) {
-        float v[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) v[j] = 0.f;
-        if (run_ok[mu][q]) load_run<XF32, CH>(xsrc, uoff + lane_off[mu][q], v);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) r.v[mu][q * CH + j] = v[j];
-      }
-  };
-  // fp16 operand: bf16 values convert exactly; fp32 values are split into a
-  // high part (reduction index < G) and a low part (index >= G)
-  auto to_operand = [&](const Raw& r, OpT* Bv) {
-#pragma unroll
-    for (int mu = 0; mu < NMF; ++mu) {
-#pragma unroll
-      for (int j = 0; j < KSTEP; ++j) {
-        const int kap = mu * MF + kc * KSTEP + j;
-        const float v = r.v[mu][j];
-        const _Float16 hi = (_Float16)v;
-        Bv[mu][j] = (XF32 && kap >= G && kap < KD) ? (_Float16)(v - (float)hi) : hi;
-      }
-    }
   };
 
   // software pipeline over units: the raw loads of unit u+3 are issued while
@@ -177,57 +179,70 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   load_raw(u0, rb[0]);
   load_raw(u0 + 1, rb[1]);
   load_raw(u0 + 2, rb[2]);
+  typedef float float16v __attribute__((ext_vector_type(16)));
   auto do_unit = [&](int u, Raw& cur, Raw& nxt) {
-    OpT Bv[NMF];
+    half8v Bv[NMF];
     to_operand(cur, Bv);
     load_raw(u + 3, nxt);
-    const int tok = u >> LUPT, gb = u & (UPT - 1);
+    const int v = u * 32 + col;
+    const bool vok = v < nvec;
+    const int vc = vok ? v : nvec - 1;
+    const int tok = vc >> ln, g = vc & (n - 1);
     const int slot = p.slot_mapping[tok];
-    // ---- scores against all entries: per 16-entry tile the lane sees 4
-    //      entries (rows 4*kc .. 4*kc+3) of its vector.  It keeps the best
-    //      tile (strict compare in increasing tile order) and that tile's four
-    //      scores; the lowest row holding the maximum is resolved at the end,
-    //      so the whole search takes the lowest index on exact ties.
-    float best = -INFINITY, bd0 = 0.f, bd1 = 0.f, bd2 = 0.f, bd3 = 0.f;
+    // ---- scores against all entries: per 32-entry tile a lane holds 16
+    //      entries (rows 8q + 4*hf + s) of its vector.  It keeps the best tile
+    //      (strict compare of the tile maxima in increasing tile order) and
+    //      that tile's 16 scores; the lowest row holding the maximum is
+    //      resolved at the end, so the search takes the lowest index on ties.
+    float best = -INFINITY;
     int btile = 0;
+    float16v bd;
+    // opaque per-unit base: keeps the accumulator-input reads inside the unit
+    int hbase = hf * 64;
+    __asm__ __volatile__("" : "+v"(hbase));
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-      float4v d = Cin[t];
+      const uint8_t* hp = (const uint8_t*)hsl + t * 128 + hbase;
+      const float4v c0 = *(const float4v*)hp, c1 = *(const float4v*)(hp + 16);
+      const float4v c2 = *(const float4v*)(hp + 32), c3 = *(const float4v*)(hp + 48);
+      float16v d = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
+                    c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
 #pragma unroll
-      for (int mu = 0; mu < NMF; ++mu) {
-        if constexpr (MF == 32) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t][mu], Bv[mu], d, 0, 0, 0);
-        else d = __builtin_amdgcn_mfma_f32_16x16x16f16(A[t][mu], Bv[mu], d, 0, 0, 0);
-      }
-      float m3 = __builtin_fmaxf(__builtin_fmaxf(d.x, d.y), d.z);
-      m3 = __builtin_fmaxf(m3, d.w);
-      const bool better = m3 > best;
-      best = better ? m3 : best;
+      for (int mu = 0; mu < NMF; ++mu) d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[t][mu], Bv[mu], d, 0, 0, 0);
+      float m = __builtin_fmaxf(__builtin_fmaxf(d[0], d[1]), d[2]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, d[3]), d[4]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, d[5]), d[6]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, d[7]), d[8]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, d[9]), d[10]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, d[11]), d[12]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, d[13]), d[14]);
+      m = __builtin_fmaxf(m, d[15]);
+      const bool better = m > best;
+      best = better ? m : best;
       btile = better ? t : btile;
-      bd0 = better ? d.x : bd0;
-      bd1 = better ? d.y : bd1;
-      bd2 = better ? d.z : bd2;
-      bd3 = better ? d.w : bd3;
-    }
-    const int r = bd0 == best ? 0 : (bd1 == best ? 1 : (bd2 == best ? 2 : 3));
-    int bidx = 16 * btile + 4 * kc + r;
-    // ---- merge the four lanes holding the same vector (lower index on ties)
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float ob = __shfl_xor(best, off);
-      const int oi = __shfl_xor(bidx, off);
+      for (int r = 0; r < 16; ++r) bd[r] = better ? d[r] : bd[r];
+    }
+    int rr = 15;
+#pragma unroll
+    for (int r = 14; r >= 0; --r) rr = bd[r] == best ? r : rr;
+    int bidx = 32 * btile + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+    // ---- merge the two lanes holding the same vector (lower index on ties)
+    {
+      const float ob = __shfl_xor(best, 32);
+      const int oi = __shfl_xor(bidx, 32);
       const bool take = ob > best || (ob == best && oi < bidx);
-      best = take ? ob : best;
       bidx = take ? oi : bidx;
     }
     // ---- write the code into its row slot
     uint8_t* row = p.cache + (int64_t)beta * p.block_stride +
-                   ((((size_t)(slot >> p.log2P) * H + h) * 2 + kv) * P + (slot & (P - 1))) * R;
-    const int sl = slot_of(gb * 16 + col);
+                   ((((size_t)(slot >> p.log2P) * H + hd) * 2 + kv) * P + (slot & (P - 1))) * R;
+    const int sl = slot_of(g);
     if constexpr (BITS == 8) {
-      if (kc == 0) row[sl] = (uint8_t)bidx;
+      if (hf == 0 && vok) row[sl] = (uint8_t)bidx;
     } else {
       const int other = __shfl_xor(bidx, 1);
-      if (kc == 0 && (col & 1) == 0) row[sl >> 1] = (uint8_t)((bidx & 15) | ((other & 15) << 4));
+      if (hf == 0 && vok && (col & 1) == 0) row[sl >> 1] = (uint8_t)((bidx & 15) | ((other & 15) << 4));
     }
   };
   int u = u0;
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
 
 template <int G, int C, bool XF32, int BITS>
 static hipError_t launch_encode_t(const EncodeParams& p, int n_blocks, hipStream_t s) {
-  dim3 grid(p.n_tok_groups, n_blocks * 2 * p.H_kv);
+  dim3 grid(p.n_unit_groups, n_blocks * 2 * p.H_kv);
   hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -46,8 +46,8 @@ struct EncodeParams {
   uint8_t* cache;             // cache of the first block
   int64_t block_stride;
   int n_tok, H_kv, D, c, Tc, K, log2P;
-  int tok_per_wave;
-  int n_tok_groups;           // ceil(n_tok / (4 * tok_per_wave))
+  int units_per_wave;         // units of 32 consecutive (token, group) vectors per wave
+  int n_unit_groups;          // ceil(units / (4 * units_per_wave)), the grid's x extent
 };
 
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
