@@ -217,11 +217,14 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       m = __builtin_fmaxf(__builtin_fmaxf(m, d[11]), d[12]);
       m = __builtin_fmaxf(__builtin_fmaxf(m, d[13]), d[14]);
       m = __builtin_fmaxf(m, d[15]);
-      const bool better = m > best;
-      best = better ? m : best;
-      btile = better ? t : btile;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bd[r] = better ? d[r] : bd[r];
+      // a new best tile is rare after the first few: a masked branch copies
+      // the scores (64-bit moves) instead of selecting all 16 every tile
+      if (m > best) {
+        __asm__ __volatile__("");          // keeps this a masked branch (no selects)
+        best = m;
+        btile = t;
+        bd = d;
+      }
     }
     int rr = 15;
 #pragma unroll
