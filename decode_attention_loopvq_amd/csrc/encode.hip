@@ -8,20 +8,27 @@
 // argmin_r ||z - e_r||^2 (lowest r on ties), written into the paged index row.
 //
 // MI355X mapping:
-//  * argmin ||z - e||^2 = argmax (z.e - 0.5*||e||^2): the dot products are one
-//    fp16 MFMA per 16 entries x 16 vectors, with -0.5*||e||^2 loaded as the
-//    accumulator input, so the distance needs no VALU work beyond the argmax.
+//  * argmin ||z - e||^2 = argmax (z.e - 0.5*||e||^2): the dot products are
+//    32x32x16 fp16 MFMAs, one tile of 32 entries x 32 vectors, with
+//    -0.5*||e||^2 (read from LDS) as the accumulator input, so the distance
+//    needs no VALU work beyond the argmax.
 //  * The MFMA reduction index runs over the coupled coordinates in loop-major
 //    order (kappa = m*c + i) on both operands, so a lane's operand is c
 //    contiguous channels of one loop step (one 8- or 16-byte load).  bf16
 //    inputs convert to fp16 exactly inside fp16's normal range; fp32 inputs
 //    are split into an fp16 high and low part placed side by side along the
 //    reduction index (against two copies of the entry).
-//  * Rows of the MFMA are codebook entries, columns are vectors: a lane sees 4
-//    entries of one vector per MFMA and keeps a running (best, index) with a
-//    strict compare in increasing entry order (lowest index on ties); the four
-//    lanes that share a vector merge at the end with a lexicographic compare.
-//  * The whole codebook tile set stays in registers for the life of the wave.
+//  * A wave scores units of 32 consecutive (token, group) vectors; lane
+//    (hf, col) holds vector col and 16 of every tile's 32 entries.  It keeps
+//    the tile with the largest maximum (strict compare in increasing tile
+//    order) and copies that tile's scores only when the best tile changes;
+//    the lowest row at the maximum is found once per unit, and the two lanes
+//    of a vector merge with a lexicographic compare (lowest index on ties).
+//  * The whole codebook tile set stays in registers for the life of the wave;
+//    the raw input loads run three units ahead of the scoring.
+//  * The argmax is exact, so it costs VALU work per score (a three-input max
+//    per two scores); that VALU work, not the MFMA rate, bounds the kernel.
+
 #include <type_traits>
 
 #include "common.h"
