@@ -342,6 +342,65 @@ def decode_attention(q: np.ndarray, cache_block: np.ndarray, block_table_row: np
     return o, lse
 
 
+def gather_rows_at(cache: np.ndarray, block_table_row: np.ndarray, pos: np.ndarray, h: int,
+                   kv: int) -> np.ndarray:
+    """Rows [len(pos), R] of the logical tokens at positions pos of one request."""
+    P = cache.shape[3]
+    p = np.asarray(pos, dtype=np.int64)
+    pages = np.asarray(block_table_row, dtype=np.int64)[p // P]
+    return cache[pages, h, kv, p % P, :]
+
+
+# --------------------------------------------------------------------------
+# bf16 sink and recent window  [P1 section "System implementation": the first
+#   n_s tokens and the most recent n_r tokens of a request stay in bf16 and
+#   all others are codes; at loop step t one kernel attends to the bf16 pages
+#   and another to the quantised pages, and the partials of both are merged by
+#   their logsumexp, which is one softmax over every cached token]
+# --------------------------------------------------------------------------
+def decode_attention_window(q: np.ndarray, cache_block: np.ndarray, block_table_row: np.ndarray,
+                            n: int, n_sink: int, win_start: int, k_bf: np.ndarray, v_bf: np.ndarray,
+                            cb_block: np.ndarray, t: int, Tc: int, c: int, bits: int, base: float,
+                            sm_scale: float | None = None):
+    """Decode attention of one request whose cache mixes bf16 tokens and codes.
+
+    Positions [0, n_sink) (the sink) and [win_start, n) (the recent window)
+    keep their pre-RoPE keys and values in bf16: k_bf, v_bf [n, H_kv, D]
+    (float64 holding the bf16 values; only the rows of those positions are
+    read).  Positions [n_sink, win_start) are codes in cache_block, looked up
+    through block_table_row exactly as in decode_attention.  Every key is
+    rotated at its own position and one softmax runs over all n tokens.
+    Returns (o [H_q, D], lse [H_q]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H_q, D = q.shape
+    H_kv = cache_block.shape[1]
+    grp = H_q // H_kv
+    assert 0 <= n_sink <= win_start <= n
+    m = (t - 1) % Tc
+    sm_scale = 1.0 / np.sqrt(D) if sm_scale is None else sm_scale
+    ng = D // c
+    qpos = np.arange(n_sink, win_start)
+    bpos = np.concatenate([np.arange(n_sink), np.arange(win_start, n)]).astype(np.int64)
+    k_bf = np.asarray(k_bf, dtype=np.float64)
+    v_bf = np.asarray(v_bf, dtype=np.float64)
+    o = np.zeros((H_q, D))
+    lse = np.zeros(H_q)
+    for h in range(H_kv):
+        k = np.empty((n, D))
+        v = np.empty((n, D))
+        ki = slots_to_groups(unpack_rows(gather_rows_at(cache_block, block_table_row, qpos, h, 0), bits, ng))
+        vi = slots_to_groups(unpack_rows(gather_rows_at(cache_block, block_table_row, qpos, h, 1), bits, ng))
+        k[qpos] = rebuild(ki, cb_block[h, 0], Tc, c, m)
+        v[qpos] = rebuild(vi, cb_block[h, 1], Tc, c, m)
+        k[bpos] = k_bf[bpos, h]
+        v[bpos] = v_bf[bpos, h]
+        krot = rope(k, np.arange(n), base)
+        for j in range(h * grp, (h + 1) * grp):
+            o[j], lse[j] = attention(q[j], krot, v, sm_scale)
+    return o, lse
+
+
 def build_index_cache(xk: np.ndarray, xv: np.ndarray, cb: np.ndarray, Tc: int, c: int,
                       bits: int, slots: np.ndarray, num_pages: int, page_size: int,
                       method: str = "direct"):

@@ -320,3 +320,101 @@ def test_row_order_hand_worked():
     np.testing.assert_array_equal(rows[0], ex["bytes"])
     back = oracle.slots_to_groups(oracle.unpack_rows(rows, 4, codes.shape[1]))
     np.testing.assert_array_equal(back, codes)
+
+
+# ---------------------------------------------------------------- bf16 sink and recent window
+def _rope_complex(x, pos, base):
+    # rotate-half RoPE written as a complex rotation (an independent form)
+    D = x.shape[1]
+    theta = base ** (-2.0 * np.arange(D // 2) / D)
+    z = (x[:, :D // 2] + 1j * x[:, D // 2:]) * np.exp(1j * np.asarray(pos)[:, None] * theta[None, :])
+    return np.concatenate([z.real, z.imag], axis=1)
+
+
+def _sdpa(q, k, v):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None, None, :], torch.tensor(k)[None, None],
+        torch.tensor(v)[None, None])[0, 0, 0].numpy()
+
+
+def _lossless_window_case(seed):
+    # values on a 1/8 grid in [-4, 4): exact in bf16 and in fp16.  The
+    # codebook of each (head, K|V) holds every coupled vector of the data plus
+    # far-away fillers, so the codes rebuild the data exactly.
+    rng = np.random.default_rng(seed)
+    T, Tc, c, D, N, H, bits, P = 4, 4, 4, 32, 24, 2, 8, 8
+    xk = rng.integers(-32, 32, size=(T, N, H, D)) / 8.0
+    xv = rng.integers(-32, 32, size=(T, N, H, D)) / 8.0
+    cb = np.zeros((1, H, 2, 256, c * Tc), dtype=np.float16)
+    for h in range(H):
+        for kv, x in enumerate((xk, xv)):
+            z = oracle.coupled_vectors(x[:, :, h, :], Tc, c, 0).reshape(-1, c * Tc)
+            fill = 100.0 + np.arange(256 - len(z))[:, None] + rng.random((256 - len(z), c * Tc))
+            cb[0, h, kv] = np.concatenate([z, fill]).astype(np.float16)
+    npg = N // P
+    bt = rng.permutation(npg).astype(np.int32)[None, :]
+    slots = synth.slot_mapping_for(bt, 0, N, P)
+    caches, ties, _ = oracle.build_index_cache(xk, xv, cb, Tc, c, bits, slots, npg, P)
+    assert ties == 0
+    return dict(xk=xk, xv=xv, cb=cb, bt=bt, cache=caches[0], Tc=Tc, c=c, bits=bits, N=N, H=H, D=D, T=T)
+
+
+@pytest.mark.parametrize("n_sink,win_start", [(0, 24), (8, 16), (0, 0), (24, 24), (8, 8), (16, 24)])
+def test_window_lossless_cache_is_dense_rope_attention(n_sink, win_start):
+    # whatever split of the positions into bf16 and codes, a lossless cache
+    # gives ordinary attention over the rotated original keys
+    g = _lossless_window_case(11)
+    rng = np.random.default_rng(12)
+    for t in range(1, g["T"] + 1):
+        q = rng.standard_normal((g["H"], g["D"]))
+        o, lse = oracle.decode_attention_window(q, g["cache"], g["bt"][0], g["N"], n_sink, win_start,
+                                                g["xk"][t - 1], g["xv"][t - 1], g["cb"][0], t, g["Tc"],
+                                                g["c"], g["bits"], 1e4)
+        for h in range(g["H"]):
+            krot = _rope_complex(g["xk"][t - 1, :, h, :], np.arange(g["N"]), 1e4)
+            want = _sdpa(q[h], krot, g["xv"][t - 1, :, h, :])
+            np.testing.assert_allclose(o[h], want, rtol=0, atol=1e-12)
+            s = (krot @ q[h]) / np.sqrt(g["D"])
+            assert abs(lse[h] - scipy.special.logsumexp(s)) < 1e-12
+
+
+def test_window_reads_bf16_rows_only_at_bf16_positions():
+    # garbage codes under bf16 positions and garbage bf16 rows under coded
+    # positions change nothing; the bf16 rows that are read are used as given
+    g = _lossless_window_case(13)
+    rng = np.random.default_rng(14)
+    n_sink, win_start, t = 8, 16, 3
+    N, H, D = g["N"], g["H"], g["D"]
+    q = rng.standard_normal((H, D))
+    cache = g["cache"].copy()
+    bpos = np.r_[0:n_sink, win_start:N]
+    P = cache.shape[3]
+    for p in bpos:
+        cache[g["bt"][0, p // P], :, :, p % P, :] = rng.integers(0, 256, size=cache.shape[-1])
+    kb = g["xk"][t - 1].copy()
+    vb = g["xv"][t - 1].copy()
+    kb[n_sink:win_start] = rng.standard_normal((win_start - n_sink, H, D))
+    vb[n_sink:win_start] = rng.standard_normal((win_start - n_sink, H, D))
+    delta = rng.standard_normal((len(bpos), H, D))
+    kb[bpos] += delta
+    o, _ = oracle.decode_attention_window(q, cache, g["bt"][0], N, n_sink, win_start, kb, vb, g["cb"][0],
+                                          t, g["Tc"], g["c"], g["bits"], 1e4)
+    for h in range(H):
+        k = g["xk"][t - 1, :, h, :].copy()
+        k[bpos] += delta[:, h, :]
+        want = _sdpa(q[h], _rope_complex(k, np.arange(N), 1e4), g["xv"][t - 1, :, h, :])
+        np.testing.assert_allclose(o[h], want, rtol=0, atol=1e-12)
+
+
+def test_window_without_bf16_tokens_is_the_quantised_decode():
+    rng = np.random.default_rng(15)
+    H_kv, grp, D, c, Tc, bits, N, P = 2, 2, 32, 4, 4, 8, 40, 8
+    cache = rng.integers(0, 256, size=(5, H_kv, 2, P, D // c), dtype=np.uint8)
+    bt = np.array([3, 1, 4, 0, 2], dtype=np.int32)
+    cbb = rng.standard_normal((H_kv, 2, 256, c * Tc)).astype(np.float16)
+    q = rng.standard_normal((H_kv * grp, D))
+    junk = rng.standard_normal((N, H_kv, D))
+    o, lse = oracle.decode_attention_window(q, cache, bt, N, 0, N, junk, junk, cbb, 2, Tc, c, bits, 1e4)
+    o2, lse2 = oracle.decode_attention(q, cache, bt, N, cbb, 2, Tc, c, bits, 1e4)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
