@@ -49,6 +49,11 @@ class loopvq_dims(ctypes.Structure):
         return self.D // self.c * self.bits // 8
 
 
+class loopvq_bf16_window(ctypes.Structure):
+    _fields_ = [("kv", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("n_sink", ctypes.c_void_p), ("win_start", ctypes.c_void_p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -85,13 +90,18 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, P]
         L.loopvq_decode_combine.restype = ctypes.c_int
         L.loopvq_decode_combine.argtypes = [D, I, P, I, P, P, P, ctypes.c_size_t, P]
+        L.loopvq_decode_attn_window.restype = ctypes.c_int
+        L.loopvq_decode_attn_window.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I,
+                                                ctypes.POINTER(loopvq_bf16_window), ctypes.c_float,
+                                                P, P, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
 
 EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_slices",
             "loopvq_rope_table", "loopvq_rope_table_floats", "loopvq_encode", "loopvq_decode_workspace_bytes",
-            "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine")
+            "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine",
+            "loopvq_decode_attn_window")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -227,3 +237,45 @@ def loopvq_decode_combine(dims: loopvq_dims, B: int, seq_lens: torch.Tensor, max
     _check(lib().loopvq_decode_combine(ctypes.byref(dims), int(B), _ptr(seq_lens), int(max_seq_len), _ptr(out),
                                        _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream()),
            "loopvq_decode_combine")
+
+
+def loopvq_decode_attn_window(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: torch.Tensor,
+                              slices: torch.Tensor, rope_table: torch.Tensor, block_table: torch.Tensor,
+                              seq_lens: torch.Tensor, max_seq_len: int, kv_bf16: torch.Tensor,
+                              page_table: torch.Tensor, n_sink: torch.Tensor, win_start: torch.Tensor,
+                              sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              max_pos: Optional[int] = None):
+    """Decode attention over coded pages plus bf16 sink / recent-window pages.
+
+    kv_bf16 [num_pages][H_kv][2][8][D] bf16 pages of loop step t; page_table
+    [B][max_pages] int32 (bf16 token u of a request in page u // 8, slot u % 8);
+    n_sink, win_start [B] int32.  Returns (out, lse).
+    """
+    iodt = torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+    _need(q, iodt, "q"); _need(index_cache, torch.uint8, "index_cache")
+    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
+    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
+    _need(kv_bf16, torch.bfloat16, "kv_bf16"); _need(page_table, torch.int32, "page_table")
+    _need(n_sink, torch.int32, "n_sink"); _need(win_start, torch.int32, "win_start")
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.H_q, dims.D), dtype=iodt, device=q.device)
+    _need(out, iodt, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if max_pos is None:
+        raise ValueError("max_pos (positions covered by rope_table) is required")
+    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+    win = loopvq_bf16_window(kv_bf16.data_ptr(), page_table.data_ptr(),
+                             page_table.shape[1] if page_table.dim() == 2 else 0,
+                             n_sink.data_ptr(), win_start.data_ptr())
+    _check(lib().loopvq_decode_attn_window(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
+                                           _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
+                                           int(max_pages), _ptr(seq_lens), int(max_seq_len), ctypes.byref(win),
+                                           float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                           int(workspace.numel()), _stream()), "loopvq_decode_attn_window")
+    return out, lse

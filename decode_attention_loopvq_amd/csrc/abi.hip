@@ -42,6 +42,8 @@ int check_dims(const loopvq_dims* d) {
 struct DecodePlan {
   int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid, shared_rope;
   size_t n_part, bytes_o, bytes_lse;
+  size_t bytes_wo, bytes_wl;   // bf16-token partials: one per (KV head, pair)
+  size_t total() const { return bytes_o + bytes_lse + bytes_wo + bytes_wl; }
 };
 
 // A wave serves one duo of (request, query head) pairs (2i, 2i+1) over one
@@ -74,6 +76,8 @@ DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   pl.n_part = (size_t)d->H_kv * std::max(pl.n_pairs, 1) * pl.n_chunks;
   pl.bytes_o = align256(pl.n_part * d->D * sizeof(float));
   pl.bytes_lse = align256(pl.n_part * sizeof(float));
+  pl.bytes_wo = align256((size_t)d->H_kv * std::max(pl.n_pairs, 1) * d->D * sizeof(float));
+  pl.bytes_wl = align256((size_t)d->H_kv * std::max(pl.n_pairs, 1) * sizeof(float));
   return pl;
 }
 
@@ -183,7 +187,7 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, i
 size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {
   if (check_dims(dims) != LOOPVQ_OK || B < 0 || max_seq_len < 0) return 0;
   const DecodePlan pl = plan_decode(dims, B, max_seq_len);
-  return pl.bytes_o + pl.bytes_lse;
+  return pl.total();
 }
 
 static int check_decode_common(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {
@@ -194,11 +198,15 @@ static int check_decode_common(const loopvq_dims* dims, int32_t B, int32_t max_s
   return LOOPVQ_OK;
 }
 
-int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
-                        const uint8_t* index_cache, const void* slices, const float* rope_table,
-                        int32_t max_pos, const int32_t* block_table, int32_t max_pages,
-                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// the split pass over the coded positions [seq_lo[b], seq_end[b]) of each
+// request (seq_lo null: from 0)
+static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                      const uint8_t* index_cache, const void* slices, const float* rope_table,
+                      int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                      const int32_t* seq_lens, const int32_t* seq_lo, int32_t max_seq_len, float sm_scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_decode_common(dims, B, max_seq_len);
   if (st != LOOPVQ_OK) return st;
   if (t < 1 || t > dims->T || max_pos < 0 || max_pages < 0) return LOOPVQ_ERR_INVALID_ARG;
@@ -209,7 +217,7 @@ int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const voi
     return LOOPVQ_ERR_INVALID_ARG;
   if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
   const DecodePlan pl = plan_decode(dims, B, max_seq_len);
-  if (workspace_bytes < pl.bytes_o + pl.bytes_lse) return LOOPVQ_ERR_WORKSPACE;
+  if (workspace_bytes < pl.total()) return LOOPVQ_ERR_WORKSPACE;
 
   DecodeParams p{};
   p.q = q;
@@ -218,6 +226,7 @@ int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const voi
   p.rope = rope_table;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
+  p.seq_lo = seq_lo;
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace + pl.bytes_o);
   p.B = B;
@@ -240,19 +249,24 @@ int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const voi
                                         pl.grid, stream));
 }
 
-int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq_lens, int32_t max_seq_len,
-                          void* out, float* lse, const void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+// the combine pass; win_o / win_lse: the bf16-token partials, or null
+static int combine_impl(const loopvq_dims* dims, int32_t B, const int32_t* seq_lens, int32_t max_seq_len,
+                        void* out, float* lse, const void* workspace, size_t workspace_bytes,
+                        bool with_window, hipStream_t stream) {
   int st = check_decode_common(dims, B, max_seq_len);
   if (st != LOOPVQ_OK) return st;
   if (B == 0) return LOOPVQ_OK;
   if (!seq_lens || !out || !workspace) return LOOPVQ_ERR_INVALID_ARG;
   if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
   const DecodePlan pl = plan_decode(dims, B, max_seq_len);
-  if (workspace_bytes < pl.bytes_o + pl.bytes_lse) return LOOPVQ_ERR_WORKSPACE;
+  if (workspace_bytes < pl.total()) return LOOPVQ_ERR_WORKSPACE;
   CombineParams cp{};
   cp.part_o = (const float*)workspace;
   cp.part_lse = (const float*)((const char*)workspace + pl.bytes_o);
+  if (with_window) {
+    cp.win_o = (const float*)((const char*)workspace + pl.bytes_o + pl.bytes_lse);
+    cp.win_lse = (const float*)((const char*)workspace + pl.bytes_o + pl.bytes_lse + pl.bytes_wo);
+  }
   cp.seq_lens = seq_lens;
   cp.out = out;
   cp.lse = lse;
@@ -264,6 +278,23 @@ int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq
   cp.Lc = pl.Lc;
   cp.max_seq_len = max_seq_len;
   return hip_status(launch_decode_combine(dims->D, dims->io_dtype == LOOPVQ_DTYPE_BF16, cp, stream));
+}
+
+extern "C" {
+
+int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                        const uint8_t* index_cache, const void* slices, const float* rope_table,
+                        int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return split_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages, seq_lens,
+                    nullptr, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+}
+
+int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq_lens, int32_t max_seq_len,
+                          void* out, float* lse, const void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return combine_impl(dims, B, seq_lens, max_seq_len, out, lse, workspace, workspace_bytes, false, stream);
 }
 
 int loopvq_decode_attn(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
@@ -278,6 +309,52 @@ int loopvq_decode_attn(const loopvq_dims* dims, int32_t t, int32_t B, const void
                            seq_lens, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
   if (st != LOOPVQ_OK) return st;
   return loopvq_decode_combine(dims, B, seq_lens, max_seq_len, out, lse, workspace, workspace_bytes, stream);
+}
+
+int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                              const uint8_t* index_cache, const void* slices, const float* rope_table,
+                              int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t max_seq_len, const loopvq_bf16_window* window,
+                              float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  int st = check_decode_common(dims, B, max_seq_len);
+  if (st != LOOPVQ_OK) return st;
+  if (window == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  if (t < 1 || t > dims->T || max_pos < 0 || max_pages < 0 || window->max_pages < 1) return LOOPVQ_ERR_INVALID_ARG;
+  if (max_seq_len > max_pos || (long long)max_seq_len > (long long)max_pages * dims->page_size)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (B == 0) return LOOPVQ_OK;
+  if (!q || !index_cache || !slices || !rope_table || !block_table || !seq_lens || !out || !workspace)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (!window->kv || !window->page_table || !window->n_sink || !window->win_start) return LOOPVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)window->kv & 15) != 0 || ((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  const DecodePlan pl = plan_decode(dims, B, max_seq_len);
+  if (workspace_bytes < pl.total()) return LOOPVQ_ERR_WORKSPACE;
+  // coded positions [n_sink, win_start)
+  st = split_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages,
+                  window->win_start, window->n_sink, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+  if (st != LOOPVQ_OK) return st;
+  WindowParams wp{};
+  wp.q = q;
+  wp.kv = (const uint16_t*)window->kv;
+  wp.page_table = window->page_table;
+  wp.n_sink = window->n_sink;
+  wp.win_start = window->win_start;
+  wp.seq_lens = seq_lens;
+  wp.rope = rope_table;
+  wp.win_o = (float*)((char*)workspace + pl.bytes_o + pl.bytes_lse);
+  wp.win_lse = (float*)((char*)workspace + pl.bytes_o + pl.bytes_lse + pl.bytes_wo);
+  wp.H_kv = dims->H_kv;
+  wp.H_q = dims->H_q;
+  wp.grp = pl.grp;
+  wp.n_pairs = pl.n_pairs;
+  wp.max_pages = window->max_pages;
+  wp.max_seq_len = max_seq_len;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)dims->D);
+  wp.scale_log2 = scale * 1.4426950408889634f;
+  st = hip_status(launch_decode_window(dims->D, dims->io_dtype == LOOPVQ_DTYPE_F32, wp, B, stream));
+  if (st != LOOPVQ_OK) return st;
+  return combine_impl(dims, B, window->win_start, max_seq_len, out, lse, workspace, workspace_bytes, true, stream);
 }
 
 }  // extern "C"

@@ -151,14 +151,18 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   const int row = lane >> 4;                 // position group of this 16-lane row
   const int la = (lane >> 2) & 3, lb = lane & 3;
   // K role: quarter la, position slot lb.  V role: position slot la, quarter lb.
-  int kq[2], bq[2], len[2];
-  bool okq[2];
+  // coded positions of stream s: [lo[s], len[s]) (positions below lo[s] are
+  // a bf16 sink attended elsewhere); has[s]: the stream has coded positions
+  int kq[2], bq[2], len[2], lo[2];
+  bool okq[2], has[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     kq[s] = 2 * duo + s;
     okq[s] = item_ok && kq[s] < p.n_pairs;
     bq[s] = okq[s] ? kq[s] / p.grp : 0;
     len[s] = okq[s] ? min(max(p.seq_lens[bq[s]], 0), p.max_seq_len) : 0;
+    lo[s] = (okq[s] && p.seq_lo != nullptr) ? min(max(p.seq_lo[bq[s]], 0), len[s]) : 0;
+    has[s] = lo[s] < len[s];
   }
   const int p0 = ch * p.Lc;
   const int lenx = max(len[0], len[1]);
@@ -237,6 +241,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     btb[s] = p.block_table + (size_t)bq[s] * p.max_pages;
   }
   const int limx = max(lim[0], lim[1]);
+  // the V lane's positions 8*rp + la (+4) of a step, relative to lo, and the
+  // span [lo, lim) of coded positions in this chunk
+  const int vrel = 8 * rp + la - lo[sv];
+  const uint32_t vspan = (uint32_t)max(lim[sv] - lo[sv], 0);
   const int glast = (max(last[0], last[1]) >> 4) << 4;   // last step-aligned group with data
   const int my_steps = active ? (limx - p0 + NT - 1) / NT : 0;   // wave-uniform
   // an opaque zero: keeps the page-id loads on the vector path, in order
@@ -250,10 +258,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   auto page_at = [&](int st, int* pg) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if constexpr (SP) pg[s] = btb[s][(min(p0 + st * NT, last[s]) >> p.log2P) + vz];
-      else pg[s] = btb[s][min(p0 + st * NT + 4 * row, last[s]) >> p.log2P];
+      if constexpr (SP) pg[s] = btb[s][(min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) + vz];
+      else pg[s] = btb[s][min(max(p0 + st * NT + 4 * row, lo[s]), last[s]) >> p.log2P];
     }
-    if constexpr (!SP) pg[NS] = btb[sv][min(p0 + st * NT + 8 * rp, last[sv]) >> p.log2P];
+    if constexpr (!SP) pg[NS] = btb[sv][min(max(p0 + st * NT + 8 * rp, lo[sv]), last[sv]) >> p.log2P];
   };
   // K rows of both streams at the lane's K position, V rows of stream sv at
   // the lane's two V positions
@@ -263,7 +271,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const uint8_t* base[2];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int page = len[s] > 0 ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
+        const int page = has[s] ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
         const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
         base[s] = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
         RowLoad<LB>::load(base[s] + kro, kw[s]);
@@ -272,11 +280,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     } else {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int page = len[s] > 0 ? raw_page[s] : 0;
+        const int page = has[s] ? raw_page[s] : 0;
         const int gs = min(p0 + st * NT + 4 * row, last[s]) & ~3;
         RowLoad<LB>::load(head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R + kro, kw[s]);
       }
-      const int page = len[sv] > 0 ? raw_page[NS] : 0;
+      const int page = has[sv] ? raw_page[NS] : 0;
       const int gs = min(p0 + st * NT + 8 * rp, last[sv]) & ~7;
       vbase = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
     }
@@ -362,8 +370,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      one token); p is rounded to fp16 for the product, and l adds the same
   //      rounded p, so the output stays an exact convex combination
   auto v_side = [&](int g0, const float* sv2) {
-    const int posa = g0 + 8 * rp + la;
-    const bool va = posa < lim[sv], vb = posa + 4 < lim[sv];
+    const int posa = g0 + vrel;
+    const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 4) < vspan;
     const float sa = va ? sv2[0] * p.scale_log2 : -INFINITY;
     const float sb = vb ? sv2[1] * p.scale_log2 : -INFINITY;
     const float smax = fmaxf(sa, sb);
@@ -480,9 +488,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     int pa[2], pcnt[2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      pa[s] = min(p0, last[s]) >> p.log2P;
-      pcnt[s] = min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX);
-      for (int i = lane; i < pcnt[s]; i += 64) plist[s * PGMAX + i] = len[s] > 0 ? btb[s][pa[s] + i] : 0;
+      pa[s] = min(max(p0, lo[s]), last[s]) >> p.log2P;
+      pcnt[s] = max(min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX), 1);
+      for (int i = lane; i < pcnt[s]; i += 64) plist[s * PGMAX + i] = has[s] ? btb[s][pa[s] + i] : 0;
     }
     if (lane == 0) wsteps[wave] = my_steps;
     __syncthreads();
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     auto page_lds = [&](int st, int* pg) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        pg[s] = plist[s * PGMAX + min((min(p0 + st * NT, last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
+        pg[s] = plist[s * PGMAX + min((min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
     };
     uint32_t kw[3][NS][LW], vw[3][2][LW];
     // one step: the rows of st+3 go to row buffer b3 = st % 3; staged pieces
@@ -623,7 +631,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   }
 }
 
-// ---- combine: one workgroup per (request, query head)
+// ---- combine: one workgroup per (request, query head).  The partials are
+//      the chunks of the coded positions and, when given, one partial over
+//      the request's bf16 tokens (sink and recent window); all are merged by
+//      their log-sum-exp.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p) {
   constexpr int SETS = 256 / D;          // partial subsets processed side by side
@@ -637,7 +648,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p) {
   const int npart = len > 0 ? (len + p.Lc - 1) / p.Lc : 0;
   const size_t base = (size_t)(h * p.n_pairs + k) * p.n_chunks;
   const int tid = threadIdx.x;
-  float M = -INFINITY;
+  const size_t wpart = (size_t)h * p.n_pairs + k;
+  const float wle = p.win_lse != nullptr ? p.win_lse[wpart] : -INFINITY;
+  float M = tid == 0 ? wle : -INFINITY;
   for (int i = tid; i < npart; i += 256) M = fmaxf(M, p.part_lse[base + i]);
   red_m[tid] = M;
   __syncthreads();
@@ -655,6 +668,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p) {
       const float w = le == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(le - M);
       W += w;
       o = fmaf(w, p.part_o[(base + i) * D + d], o);
+    }
+    if (set == 0 && wle != -INFINITY) {
+      const float w = __builtin_amdgcn_exp2f(wle - M);
+      W += w;
+      o = fmaf(w, p.win_o[wpart * D + d], o);
     }
   }
   red_o[tid] = o;

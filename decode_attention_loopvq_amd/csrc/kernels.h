@@ -13,7 +13,8 @@ struct DecodeParams {
   const void* slices;         // slice of the step: [H_kv][2][K][C] fp16
   const float* rope;          // [max_pos][D/16][4][4]
   const int32_t* block_table; // [B][max_pages]
-  const int32_t* seq_lens;    // [B]
+  const int32_t* seq_lens;    // [B] end of each request's coded positions
+  const int32_t* seq_lo;      // [B] first coded position (bf16 sink before it), or null for 0
   float* part_o;              // [H_kv][n_pairs][n_chunks][D]
   float* part_lse;            // [H_kv][n_pairs][n_chunks], log2 domain
   int B, H_kv, H_q, grp, max_pages, log2P;
@@ -31,10 +32,27 @@ struct DecodeParams {
 struct CombineParams {
   const float* part_o;
   const float* part_lse;
+  const float* win_o;         // [H_kv][n_pairs][D] bf16-token partials, or null
+  const float* win_lse;       // [H_kv][n_pairs], log2 domain
   const int32_t* seq_lens;
   void* out;
   float* lse;
   int B, H_q, grp, n_pairs, n_chunks, Lc, max_seq_len;
+};
+
+// attention over the bf16 tokens of each request (sink and recent window)
+struct WindowParams {
+  const void* q;              // [B][H_q][D] bf16 or fp32
+  const uint16_t* kv;         // bf16 pages [num_pages][H_kv][2][8][D], pre-RoPE K and V
+  const int32_t* page_table;  // [B][max_pages]: bf16 token u sits in page u/8, slot u%8
+  const int32_t* n_sink;      // [B] sink tokens, positions [0, n_sink)
+  const int32_t* win_start;   // [B] first position of the recent window
+  const int32_t* seq_lens;    // [B] tokens per request; the window is [win_start, seq_len)
+  const float* rope;          // the decode kernel's RoPE table
+  float* win_o;               // [H_kv][n_pairs][D]
+  float* win_lse;             // [H_kv][n_pairs], log2 domain
+  int H_kv, H_q, grp, n_pairs, max_pages, max_seq_len;
+  float scale_log2;
 };
 
 struct EncodeParams {
@@ -53,6 +71,7 @@ struct EncodeParams {
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                hipStream_t s);
 hipError_t launch_decode_combine(int D, bool out_bf16, const CombineParams& p, hipStream_t s);
+hipError_t launch_decode_window(int D, bool qf32, const WindowParams& p, int B, hipStream_t s);
 hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_build_slices(const uint16_t* cb, uint16_t* slices, float* hsq, int n_blocks, int H_kv,
                                int K, int c, int Tc, hipStream_t s);

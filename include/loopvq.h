@@ -154,7 +154,8 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
                   uint8_t* index_cache, int64_t block_stride_bytes,
                   hipStream_t stream);
 
-/* Workspace bytes that loopvq_decode_attn needs for this batch shape. */
+/* Workspace bytes that loopvq_decode_attn and loopvq_decode_attn_window need
+ * for this batch shape. */
 size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
                                      int32_t max_seq_len);
 
@@ -212,6 +213,58 @@ int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq
                           int32_t max_seq_len, void* out, float* lse,
                           const void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * The bf16 pages of a request: its attention sink and its recent window.
+ * [LoopVQ paper, section "System implementation", cache layout: the first
+ * n_s tokens and the most recent tokens of a request stay in bf16, in pages of
+ * 8 tokens, and every other token is coded; the window is coded a page at a
+ * time as it moves on, so its keys are kept before RoPE.]
+ *   kv          bf16 pages of the loop step being attended:
+ *               [num_pages][H_kv][2][8][D], index 0 the pre-RoPE key, 1 the
+ *               value; 16-byte aligned.
+ *   page_table  [B][max_pages] int32.  Number the bf16 tokens of request b
+ *               u = 0, 1, ...: first its sink positions 0 .. n_sink-1, then
+ *               its window positions win_start .. seq_len-1.  Token u sits in
+ *               page page_table[b][u / 8], slot u % 8.
+ *   n_sink      [B] int32 sink tokens of each request (positions [0, n_sink)).
+ *   win_start   [B] int32 first position of the recent window; positions
+ *               [win_start, seq_len) are bf16.
+ * Requires 0 <= n_sink[b] <= win_start[b] <= seq_lens[b] and
+ * ceil((n_sink + seq_len - win_start) / 8) <= max_pages (device values, not
+ * checked on the host; out-of-order values are clamped into that order).
+ */
+typedef struct loopvq_bf16_window {
+  const void* kv;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* n_sink;
+  const int32_t* win_start;
+} loopvq_bf16_window;
+
+/*
+ * Decode attention at loop step t over a cache that mixes bf16 pages (sink
+ * and recent window) with coded pages.  [LoopVQ paper, section "System
+ * implementation", attention: one kernel attends to the bf16 pages and
+ * another to the quantised pages, and their split partials are merged by the
+ * logsumexp of their scores, which is one softmax over every token.]
+ * Positions [n_sink, win_start) of request b are read as codes through
+ * block_table, exactly as loopvq_decode_attn reads positions [0, seq_len);
+ * block-table entries of pages that hold no coded position are never read.
+ * The other positions come from the bf16 pages; every key is rotated at its
+ * own position.  seq_lens holds the full length of each request.  Other
+ * arguments as for loopvq_decode_attn; workspace_bytes must be at least
+ * loopvq_decode_workspace_bytes(dims, B, max_seq_len).
+ */
+int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B,
+                              const void* q, const uint8_t* index_cache,
+                              const void* slices, const float* rope_table,
+                              int32_t max_pos, const int32_t* block_table,
+                              int32_t max_pages, const int32_t* seq_lens,
+                              int32_t max_seq_len,
+                              const loopvq_bf16_window* window, float sm_scale,
+                              void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -300,3 +300,60 @@ def make_kv_torch(cfg: Config, n_tok: int, seed: int, device="cuda", dtype=None)
             x[t] = (prev * sc[kv]).to(dtype)
         out.append(x)
     return out[0], out[1]
+
+
+# --------------------------------------------------------------------------
+# bf16 sink and recent window (placement only)
+# --------------------------------------------------------------------------
+def make_window(cfg: Config, seq_lens: np.ndarray, n_sink: int, n_recent: int,
+                seed: Optional[int] = None):
+    """Sink / recent-window split of each request and a random bf16 page assignment.
+
+    Request b keeps positions [0, n_sink) and [win_start, seq_len) in bf16
+    pages of 8 tokens; win_start is the largest multiple of 8 that leaves at
+    least n_recent tokens in the window (so it holds n_recent to n_recent + 7
+    tokens), and never below the sink.  Bf16 token u of a request (sink first,
+    then window) sits in page page_table[b, u // 8], slot u % 8; the physical
+    pages are a random permutation.
+    Returns (n_sink [B] int32, win_start [B] int32, page_table [B, max_pages]
+    int32, num_pages).
+    """
+    seed = (cfg.index if seed is None else seed) + 3000 + 2
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    ns = np.minimum(n_sink, lens)
+    ws = np.clip(((lens - n_recent) // 8) * 8, ns, lens)
+    nbf = ns + lens - ws
+    n_pages = (nbf + 7) // 8
+    total = int(n_pages.sum())
+    perm = rng.permutation(max(total, 1)).astype(np.int32)
+    pt = np.zeros((len(lens), max(1, int(n_pages.max(initial=0)))), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(n_pages):
+        pt[b, :n] = perm[off:off + n]
+        off += int(n)
+    return ns.astype(np.int32), ws.astype(np.int32), pt, max(total, 1)
+
+
+def window_positions(n_sink: int, win_start: int, seq_len: int) -> np.ndarray:
+    """Positions of a request's bf16 tokens u = 0, 1, ... (sink, then window)."""
+    return np.concatenate([np.arange(n_sink), np.arange(win_start, seq_len)]).astype(np.int64)
+
+
+def fill_window_pages(num_pages: int, page_table: np.ndarray, n_sink: np.ndarray, win_start: np.ndarray,
+                      seq_lens: np.ndarray, k_of, v_of, H: int, D: int) -> np.ndarray:
+    """bf16 pages [num_pages, H, 2, 8, D] (float32 holding bf16 values).
+
+    k_of(b, pos) and v_of(b, pos) return the [len(pos), H, D] pre-RoPE keys and
+    values of request b at the given positions (already bf16 values).
+    """
+    pages = np.zeros((num_pages, H, 2, 8, D), dtype=np.float32)
+    for b in range(len(seq_lens)):
+        pos = window_positions(int(n_sink[b]), int(win_start[b]), int(seq_lens[b]))
+        if len(pos) == 0:
+            continue
+        u = np.arange(len(pos))
+        pg = page_table[b, u // 8]
+        pages[pg, :, 0, u % 8, :] = k_of(b, pos)
+        pages[pg, :, 1, u % 8, :] = v_of(b, pos)
+    return pages

@@ -69,6 +69,44 @@ class GpuLayer:
                 None if lse is None else lse.cpu().numpy().astype(np.float64))
 
 
+    def decode_window(self, t, q, cache_block, block_table, seq_lens, kv_pages, page_table, n_sink, win_start,
+                      max_seq_len=None, want_lse=True):
+        q_d = q if isinstance(q, torch.Tensor) else io_tensor(self.cfg, q)
+        cache_d = cache_block if isinstance(cache_block, torch.Tensor) else to_dev(cache_block)
+        kv_d = kv_pages if isinstance(kv_pages, torch.Tensor) else to_dev(np.asarray(kv_pages, np.float32),
+                                                                          torch.bfloat16)
+        msl = int(np.max(seq_lens)) if max_seq_len is None else max_seq_len
+        lse = torch.empty((q_d.shape[0], self.cfg.H_q), dtype=torch.float32, device="cuda") if want_lse else None
+        i32 = lambda a: to_dev(np.asarray(a, dtype=np.int32))
+        out, lse = lv.loopvq_decode_attn_window(self.dims, t, q_d, cache_d, self.slices, self.rope,
+                                                i32(block_table), i32(seq_lens), msl, kv_d, i32(page_table),
+                                                i32(n_sink), i32(win_start), lse=lse, max_pos=self.max_pos)
+        torch.cuda.synchronize()
+        return (out.float().cpu().numpy().astype(np.float64),
+                None if lse is None else lse.cpu().numpy().astype(np.float64))
+
+
+def ref_decode_window(cfg, t, q, cache_block, block_table, seq_lens, cb, n_sink, win_start, kv_of,
+                      requests=None, heads=None):
+    """Oracle output with bf16 sink/window tokens; kv_of(b, h) -> (k [n, D], v [n, D]) bf16 values of
+    request b's positions (only the bf16 positions are read)."""
+    grp = cfg.H_q // cfg.H_kv
+    beta = (t - 1) // cfg.Tc
+    requests = range(len(seq_lens)) if requests is None else requests
+    heads = range(cfg.H_kv) if heads is None else heads
+    res = {}
+    for b in requests:
+        for h in heads:
+            rows = slice(h * grp, (h + 1) * grp)
+            k, v = kv_of(b, h)
+            o, lse = oracle.decode_attention_window(np.asarray(q[b], np.float64)[rows], cache_block[:, h:h + 1],
+                                                    block_table[b], int(seq_lens[b]), int(n_sink[b]),
+                                                    int(win_start[b]), k[:, None, :], v[:, None, :],
+                                                    cb[beta, h:h + 1], t, cfg.Tc, cfg.c, cfg.bits, cfg.base)
+            res[(b, h)] = (o, lse)
+    return res
+
+
 def ref_decode(cfg, t, q, cache_block, block_table, seq_lens, cb, requests=None, heads=None, sm_scale=None):
     """Oracle output for the selected requests and KV heads (query rows of those heads)."""
     grp = cfg.H_q // cfg.H_kv

@@ -97,6 +97,34 @@ def test_decode_validation_before_launch(L):
                                   FAKE, None, FAKE, 1 << 20, None) == -2
 
 
+def test_window_decode_validation_before_launch(L):
+    lib = L.lib()
+    d = _dims(L)
+    ws = L.loopvq_decode_workspace_bytes(d, 4, 1000)
+    good = L.loopvq_bf16_window(1 << 20, 1 << 20, 4, 1 << 20, 1 << 20)
+    def call(t=1, B=4, max_pos=1000, max_pages=16, max_seq_len=1000, ws_bytes=ws, win=good, ptrs=FAKE):
+        w = None if win is None else ctypes.byref(win)
+        return lib.loopvq_decode_attn_window(ctypes.byref(d), t, B, ptrs, ptrs, ptrs, ptrs, max_pos, ptrs,
+                                             max_pages, ptrs, max_seq_len, w, 0.0, ptrs, None, FAKE, ws_bytes,
+                                             None)
+    assert call(win=None) == -1
+    assert call(t=0) == -1
+    assert call(max_pos=999) == -1
+    assert call(max_pages=15) == -1
+    assert call(ptrs=None) == -1
+    assert call(ws_bytes=ws - 1) == -3
+    for bad in (L.loopvq_bf16_window(None, 1 << 20, 4, 1 << 20, 1 << 20),
+                L.loopvq_bf16_window(1 << 20, None, 4, 1 << 20, 1 << 20),
+                L.loopvq_bf16_window(1 << 20, 1 << 20, 0, 1 << 20, 1 << 20),
+                L.loopvq_bf16_window(1 << 20, 1 << 20, 4, None, 1 << 20),
+                L.loopvq_bf16_window(1 << 20, 1 << 20, 4, 1 << 20, None),
+                L.loopvq_bf16_window((1 << 20) + 2, 1 << 20, 4, 1 << 20, 1 << 20)):   # pages not 16-byte aligned
+        assert call(win=bad) == -1
+    assert call(B=0) == 0
+    # the window's partials need a larger workspace than the coded pass alone
+    assert ws > 0
+
+
 def test_encode_validation_before_launch(L):
     lib = L.lib()
     d = _dims(L)

@@ -60,3 +60,25 @@ def test_ragged_lengths_and_block_table():
     bt, n = synth.make_block_table(cfg, lens)
     used = np.concatenate([bt[b, :(l + 63) // 64] for b, l in enumerate(lens)])
     assert sorted(used.tolist()) == list(range(n))
+
+
+def test_window_split_and_pages():
+    cfg = synth.config_by_name("layer1p4b")
+    lens = np.array([1000, 1003, 5, 0, 72, 71])
+    ns, ws, pt, npg = synth.make_window(cfg, lens, 8, 64)
+    np.testing.assert_array_equal(ns, [8, 8, 5, 0, 8, 8])
+    np.testing.assert_array_equal(ws, [936, 936, 5, 0, 8, 8])
+    # the window holds n_recent to n_recent + 7 tokens where the sink leaves room
+    assert all(64 <= l - w <= 71 for l, w in zip(lens[:2], ws[:2]))
+    nbf = ns + lens - ws
+    used = np.concatenate([pt[b, :(n + 7) // 8] for b, n in enumerate(nbf)])
+    assert len(np.unique(used)) == len(used) == npg      # every physical page used once
+    pages = synth.fill_window_pages(npg, pt, ns, ws, lens,
+                                    lambda b, pos: np.broadcast_to((b * 10000 + pos)[:, None, None], (len(pos), 2, 4)),
+                                    lambda b, pos: -np.broadcast_to((b * 10000 + pos)[:, None, None], (len(pos), 2, 4)),
+                                    2, 4)
+    for b in range(len(lens)):
+        pos = synth.window_positions(int(ns[b]), int(ws[b]), int(lens[b]))
+        for u, p in enumerate(pos):
+            assert pages[pt[b, u // 8], 1, 0, u % 8, 3] == b * 10000 + p
+            assert pages[pt[b, u // 8], 0, 1, u % 8, 0] == -(b * 10000 + p)
