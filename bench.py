@@ -8,8 +8,10 @@ One step = one quantised decode-attention call (split-K kernel + combine) of
 the long-context workload at one loop step, for all KV and query heads of a
 batch of 16 requests with 32768 cached tokens each; the loop step cycles
 t = 1..4 from step to step.  The cache it reads was built beforehand by the
-GPU encoder from synthetic loop-correlated keys and values.  The encoder is
-timed separately on the prefill of the 1.4B-layer workload (8 x 4096 tokens).
+GPU encoder from synthetic loop-correlated keys and values.  Two more legs
+are reported beside the headline: the same batch with a 64-token bf16 sink
+and a 256-token bf16 recent window ("window"), and the encoder on the
+prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode").
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -152,9 +154,49 @@ def bench_decode(args, torch, np, synth, lv):
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                   "kernel": DECODE_KERNEL, "algorithmic_bytes_per_launch": algo,
                   "avg_launch_ms": round(split_avg, 5), "source_sha": sha},
-        cache=cache, bt_np=bt_np, cb=cb, qs=qs, dims=dims,
+        cache=cache, bt_np=bt_np, cb=cb, qs=qs, dims=dims, slices=slices, rope=rope, bt=bt, seq=seq,
     )
     return res
+
+
+def bench_window(args, torch, np, synth, lv, dec, n_sink=64, n_recent=256):
+    """The same 32K batch with a bf16 sink and recent window (whole call: coded split,
+    bf16-window kernel, combine)."""
+    cfg, dims, lens = dec["cfg"], dec["dims"], dec["lens"]
+    B, max_seq_len = len(lens), dec["max_seq_len"]
+    ns, ws, pt_np, n_wp = synth.make_window(cfg, lens, n_sink, n_recent)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.index + 5000)
+    kv = torch.randn((n_wp, cfg.H_kv, 2, 8, cfg.D), generator=g, device="cuda").to(torch.bfloat16)
+    pt = torch.from_numpy(pt_np).cuda()
+    ns_d = torch.from_numpy(ns).cuda()
+    ws_d = torch.from_numpy(ws).cuda()
+    out = torch.empty((B, cfg.H_q, cfg.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device="cuda")
+    wsp = torch.empty(lv.loopvq_decode_workspace_bytes(dims, B, max_seq_len), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        t = i % cfg.T + 1
+        lv.loopvq_decode_attn_window(dims, t, dec["qs"][t - 1], dec["cache"][0], dec["slices"], dec["rope"],
+                                     dec["bt"], dec["seq"], max_seq_len, kv, pt, ns_d, ws_d, out=out, lse=lse,
+                                     workspace=wsp, max_pos=max_seq_len)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbf = int((ns + lens - ws).sum())
+    return {"metric": "decode-attn cached tokens/s with a bf16 sink and recent window",
+            "value": round(float(lens.sum()) / (ms * 1e-3), 1), "unit": "cached tokens/s",
+            "ms_per_call": round(ms, 5),
+            "workload": f"{cfg.name} batch, n_sink={n_sink}, window {n_recent}..{n_recent + 7} tokens: "
+                        f"{nbf} bf16 tokens and {int(lens.sum()) - nbf} coded tokens per call",
+            "bf16_bytes_per_call": nbf * cfg.H_kv * 2 * cfg.D * 2}
 
 
 def bench_encode(args, torch, np, synth, lv):
@@ -253,6 +295,7 @@ def main():
         del src, dst
 
     dec = bench_decode(args, torch, np, synth, lv)
+    win = bench_window(args, torch, np, synth, lv, dec)
     enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
     cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
     cfg = dec["cfg"]
@@ -279,6 +322,7 @@ def main():
         "decode_split_ms": round(dec["split_avg_ms"], 5),
         "decode_combine_ms": round(dec["combine_avg_ms"], 5),
         "per_loop_step_tokens_per_s": {k: round(v, 1) for k, v in dec["per_t_tokens_per_s"].items()},
+        "window": win,
         "encode": enc,
     }
     print(json.dumps(line), flush=True)
