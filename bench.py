@@ -10,7 +10,8 @@ batch of 16 requests with 32768 cached tokens each; the loop step cycles
 t = 1..4 from step to step.  The cache it reads was built beforehand by the
 GPU encoder from synthetic loop-correlated keys and values.  Two more legs
 are reported beside the headline: the same batch with a 64-token bf16 sink
-and a 256-token bf16 recent window ("window"), and the encoder on the
+and a 256-token bf16 recent window ("window"), the decode-time coding of
+one 8-token window page per request ("page_encode"), and the encoder on the
 prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode").
 Prints one JSON line.
 """
@@ -199,6 +200,38 @@ def bench_window(args, torch, np, synth, lv, dec, n_sink=64, n_recent=256):
             "bf16_bytes_per_call": nbf * cfg.H_kv * 2 * cfg.D * 2}
 
 
+def bench_page_encode(args, torch, np, synth, lv, dec):
+    """Decode-time page encoding at the 32K batch's shape: the oldest 8-token bf16
+    window page of each of the 16 requests, coded for all loop steps at once."""
+    cfg, dims = dec["cfg"], dec["dims"]
+    B = len(dec["lens"])
+    n_pool = 8 * B
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.index + 6000)
+    pool = torch.randn((cfg.T, n_pool, cfg.H_kv, 2, 8, cfg.D), generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(cfg.index + 6001)
+    pages = rng.permutation(n_pool)[:B]
+    src = torch.from_numpy((pages[:, None] * 8 + np.arange(8)[None, :]).reshape(-1).astype(np.int32)).cuda()
+    cache = torch.zeros((B, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+    slots = torch.from_numpy((np.arange(B)[:, None] * cfg.page_size + np.arange(8)[None, :])
+                             .reshape(-1).astype(np.int32)).cuda()
+    _, hsq = lv.loopvq_build_codebook_slices(dims, dec["cb"])
+    for _ in range(args.warmup):
+        lv.loopvq_encode_pages(dims, pool, src, dec["cb"], hsq, slots, cache)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        lv.loopvq_encode_pages(dims, pool, src, dec["cb"], hsq, slots, cache)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "decode-time page encode latency", "value": round(ms * 1e3, 2), "unit": "us per call",
+            "workload": f"{B} requests x 8 tokens, {cfg.T} loop steps ({cfg.n_blocks} block), H_kv={cfg.H_kv}, "
+                        f"D={cfg.D}, c={cfg.c}, K={cfg.K}: {B * 8 * cfg.H_kv * 2 * cfg.n_groups} coupled vectors",
+            "higher_is_better": False}
+
+
 def bench_encode(args, torch, np, synth, lv):
     cfg = synth.config_by_name("layer1p4b")
     n_tok = cfg.encode_batch * cfg.encode_tokens
@@ -296,6 +329,7 @@ def main():
 
     dec = bench_decode(args, torch, np, synth, lv)
     win = bench_window(args, torch, np, synth, lv, dec)
+    penc = bench_page_encode(args, torch, np, synth, lv, dec)
     enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
     cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
     cfg = dec["cfg"]
@@ -323,6 +357,7 @@ def main():
         "decode_combine_ms": round(dec["combine_avg_ms"], 5),
         "per_loop_step_tokens_per_s": {k: round(v, 1) for k, v in dec["per_t_tokens_per_s"].items()},
         "window": win,
+        "page_encode": penc,
         "encode": enc,
     }
     print(json.dumps(line), flush=True)

@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_rope_table_floats.argtypes = [I, I]
         L.loopvq_encode.restype = ctypes.c_int
         L.loopvq_encode.argtypes = [D, I, I, I, P, P, P, P, P, P, ctypes.c_int64, P]
+        L.loopvq_encode_pages.restype = ctypes.c_int
+        L.loopvq_encode_pages.argtypes = [D, I, I, I, P, ctypes.c_int64, P, P, P, P, P, ctypes.c_int64, P]
         L.loopvq_decode_workspace_bytes.restype = ctypes.c_size_t
         L.loopvq_decode_workspace_bytes.argtypes = [D, I, I]
         L.loopvq_decode_attn.restype = ctypes.c_int
@@ -99,7 +101,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_slices",
-            "loopvq_rope_table", "loopvq_rope_table_floats", "loopvq_encode", "loopvq_decode_workspace_bytes",
+            "loopvq_rope_table", "loopvq_rope_table_floats", "loopvq_encode", "loopvq_encode_pages",
+            "loopvq_decode_workspace_bytes",
             "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine",
             "loopvq_decode_attn_window")
 
@@ -180,6 +183,28 @@ def loopvq_encode(dims: loopvq_dims, xk: torch.Tensor, xv: torch.Tensor, cb: tor
     _check(lib().loopvq_encode(ctypes.byref(dims), n_tok, first_block, n_blocks, _ptr(xk), _ptr(xv),
                                _ptr(cb), _ptr(hsq), _ptr(slot_mapping), _ptr(index_cache),
                                int(block_stride_bytes), _stream()), "loopvq_encode")
+
+
+def loopvq_encode_pages(dims: loopvq_dims, kv_pages: torch.Tensor, src_slot: torch.Tensor, cb: torch.Tensor,
+                        hsq: torch.Tensor, slot_mapping: torch.Tensor, index_cache: torch.Tensor,
+                        first_block: int = 0, n_blocks: Optional[int] = None,
+                        block_stride_bytes: Optional[int] = None) -> None:
+    """Code the tokens src_slot of bf16 page pools kv_pages [steps][num_pages][H_kv][2][8][D] (loop
+    steps of blocks first_block.. in order) into index_cache, as loopvq_encode would."""
+    _need(kv_pages, torch.bfloat16, "kv_pages"); _need(src_slot, torch.int32, "src_slot")
+    _need(cb, torch.float16, "cb"); _need(hsq, torch.float32, "hsq")
+    _need(slot_mapping, torch.int32, "slot_mapping"); _need(index_cache, torch.uint8, "index_cache")
+    if n_blocks is None:
+        n_blocks = kv_pages.shape[0] // dims.Tc
+    if kv_pages.dim() != 6 or kv_pages.shape[0] < n_blocks * dims.Tc or slot_mapping.numel() != src_slot.numel():
+        raise ValueError("encode_pages: inconsistent shapes")
+    if block_stride_bytes is None:
+        block_stride_bytes = index_cache.numel() // max(n_blocks, 1) if n_blocks > 1 else 0
+    step_stride = kv_pages[0].numel()
+    _check(lib().loopvq_encode_pages(ctypes.byref(dims), int(src_slot.numel()), first_block, n_blocks,
+                                     _ptr(kv_pages), int(step_stride), _ptr(src_slot), _ptr(cb), _ptr(hsq),
+                                     _ptr(slot_mapping), _ptr(index_cache), int(block_stride_bytes), _stream()),
+           "loopvq_encode_pages")
 
 
 def loopvq_decode_workspace_bytes(dims: loopvq_dims, B: int, max_seq_len: int) -> int:

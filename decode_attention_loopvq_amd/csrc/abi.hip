@@ -145,10 +145,13 @@ size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D) {
   return (size_t)(((int64_t)max_pos + 15) / 16 * 16) * D;
 }
 
-int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
-                  const void* xk, const void* xv, const void* cb, const float* hsq,
-                  const int32_t* slot_mapping, uint8_t* index_cache, int64_t block_stride_bytes,
-                  hipStream_t stream) {
+}  // extern "C"
+
+// shared by the dense and the paged-bf16 encode entry points
+static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
+                       const void* xk, const void* xv, const int32_t* src_slot, int64_t step_stride,
+                       const void* cb, const float* hsq, const int32_t* slot_mapping, uint8_t* index_cache,
+                       int64_t block_stride_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != LOOPVQ_OK) return st;
   const int nb_total = dims->T / dims->Tc;
@@ -162,6 +165,8 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, i
   EncodeParams p{};
   p.xk = xk;
   p.xv = xv;
+  p.src_slot = src_slot;
+  p.step_stride = step_stride;
   p.cb = (const uint16_t*)cb + (size_t)first_block * H * 2 * K * G;
   p.hsq = hsq + (size_t)first_block * H * 2 * K;
   p.slot_mapping = slot_mapping;
@@ -182,6 +187,35 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, i
   p.units_per_wave = (int)upw;
   p.n_unit_groups = (int)((units + 4 * upw - 1) / (4 * upw));
   return hip_status(launch_encode(G, dims->x_dtype == LOOPVQ_DTYPE_F32, dims->bits, p, n_blocks, stream));
+}
+
+extern "C" {
+
+int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
+                  const void* xk, const void* xv, const void* cb, const float* hsq,
+                  const int32_t* slot_mapping, uint8_t* index_cache, int64_t block_stride_bytes,
+                  hipStream_t stream) {
+  if (check_dims(dims) != LOOPVQ_OK) return check_dims(dims);
+  const int64_t step_stride = (int64_t)std::max(n_tok, 0) * dims->H_kv * dims->D;
+  return encode_impl(dims, n_tok, first_block, n_blocks, xk, xv, nullptr, step_stride, cb, hsq, slot_mapping,
+                     index_cache, block_stride_bytes, stream);
+}
+
+int loopvq_encode_pages(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
+                        const void* kv_pages, int64_t step_stride, const int32_t* src_slot, const void* cb,
+                        const float* hsq, const int32_t* slot_mapping, uint8_t* index_cache,
+                        int64_t block_stride_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != LOOPVQ_OK) return st;
+  if (dims->x_dtype != LOOPVQ_DTYPE_BF16) return LOOPVQ_ERR_UNSUPPORTED;   // the window pages are bf16
+  if (n_tok > 0 && (!kv_pages || !src_slot)) return LOOPVQ_ERR_INVALID_ARG;
+  if (n_tok > 0 && ((uintptr_t)kv_pages & 15) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (n_blocks * dims->Tc > 1 && step_stride <= 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (step_stride < 0 || step_stride % 8 != 0) return LOOPVQ_ERR_INVALID_ARG;
+  // block beta of this call reads loop steps (beta - first_block)*Tc .. of the pools
+  const void* xv = kv_pages ? (const void*)((const uint16_t*)kv_pages + 8 * dims->D) : nullptr;
+  return encode_impl(dims, n_tok, first_block, n_blocks, kv_pages, xv, src_slot, step_stride, cb, hsq,
+                     slot_mapping, index_cache, block_stride_bytes, stream);
 }
 
 size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {

@@ -36,7 +36,7 @@
 
 namespace loopvq {
 
-template <int G, int C, bool XF32, int BITS>
+template <int G, int C, bool XF32, int BITS, bool PAGED>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   constexpr int KD = XF32 ? 2 * G : G;          // reduction length (fp32: high and low halves)
   constexpr int KDP = KD < 16 ? 16 : KD;        // padded to the MFMA depth
@@ -100,7 +100,11 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   if (u0 >= u1) return;                // no work (no barrier follows)
 
   // element offset of run (mu, q) of this lane, without the token/group part
-  const size_t step_stride = (size_t)p.n_tok * H * D;
+  // element offsets: loop step (beta*Tc + m), head, token.  Dense input is
+  // [step][token][head][D]; paged bf16 input is [step][page][head][2][8][D]
+  // with token j in page src_slot[j] / 8, slot src_slot[j] % 8
+  const size_t step_stride = (size_t)p.step_stride;
+  const size_t head_stride = PAGED ? (size_t)16 * D : (size_t)D;
   size_t run_off[NMF][NRUN];
   bool run_ok[NMF][NRUN];
 #pragma unroll
@@ -111,14 +115,21 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       run_ok[mu][q] = kap < KD;
       const int kp = (XF32 && kap >= G) ? kap - G : kap;
       const int m = kp / C, i0 = kp - m * C;
-      run_off[mu][q] = (size_t)(beta * Tc + m) * step_stride + (size_t)hd * D + i0;
+      run_off[mu][q] = (size_t)(beta * Tc + m) * step_stride + (size_t)hd * head_stride + i0;
     }
   // raw input words of one unit (bf16 pairs or fp32), converted at use
   struct Raw { uint32_t w[NMF][NRUN][RW]; };
   auto load_raw = [&](int u, Raw& r) {
     const int v = min(u * 32 + col, nvec - 1);     // clamped: loads stay in bounds
     const int tok = v >> ln, g = v & (n - 1);
-    const size_t voff = (size_t)tok * H * D + (size_t)g * C;
+    size_t tbase;
+    if constexpr (PAGED) {
+      const int ss = p.src_slot[tok];
+      tbase = ((size_t)(ss >> 3) * H * 16 + (ss & 7)) * D;
+    } else {
+      tbase = (size_t)tok * H * D;
+    }
+    const size_t voff = tbase + (size_t)g * C;
 #pragma unroll
     for (int mu = 0; mu < NMF; ++mu)
 #pragma unroll
@@ -270,7 +281,15 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
 template <int G, int C, bool XF32, int BITS>
 static hipError_t launch_encode_t(const EncodeParams& p, int n_blocks, hipStream_t s) {
   dim3 grid(p.n_unit_groups, n_blocks * 2 * p.H_kv);
-  hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS>), grid, dim3(256), 0, s, p);
+  if constexpr (!XF32) {
+    // bf16 window pages (decode-time page encoding)
+    if (p.src_slot != nullptr) {
+      hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.src_slot != nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -56,8 +56,11 @@ struct WindowParams {
 };
 
 struct EncodeParams {
-  const void* xk;             // [n_blocks*Tc][n_tok][H_kv][D]
+  const void* xk;             // dense [n_blocks*Tc][n_tok][H_kv][D], or bf16 pages (see src_slot)
   const void* xv;
+  const int32_t* src_slot;    // null: dense input; else bf16 pages [step][page][H_kv][2][8][D], token j at
+                              // page src_slot[j] / 8, slot src_slot[j] % 8 (xv = xk + 8*D)
+  int64_t step_stride;        // elements between consecutive loop steps of the input
   const uint16_t* cb;         // [n_blocks][H_kv][2][K][G] fp16 of the first block
   const float* hsq;           // [n_blocks][H_kv][2][K]
   const int32_t* slot_mapping;

@@ -154,6 +154,33 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
                   uint8_t* index_cache, int64_t block_stride_bytes,
                   hipStream_t stream);
 
+/*
+ * Decode-time page encoding: code tokens held in bf16 pages (the recent
+ * window) into the paged index caches, for every loop step of the given
+ * blocks at once.  [LoopVQ paper, section "System implementation",
+ * encoding: during decoding each new token's keys and values go to the bf16
+ * window, where all its loop steps are available after the forward pass, and
+ * every delta generated tokens the oldest window page is coded across all
+ * layers and loop steps into one quantised page.]  The arithmetic and the
+ * result are those of loopvq_encode on the same values.
+ *   n_tok         tokens to code (0 is a no-op).
+ *   kv_pages      bf16 page pool of loop step first_block*Tc:
+ *                 [num_pages][H_kv][2][8][D] (index 0 the pre-RoPE key, 1 the
+ *                 value), 16-byte aligned; loop step first_block*Tc + s is the
+ *                 pool at kv_pages + s*step_stride elements.
+ *   step_stride   elements between the pools of consecutive loop steps
+ *                 (a multiple of 8; may be 0 only when n_blocks*Tc == 1).
+ *   src_slot      [n_tok] int32: page*8 + slot of each token in the pools.
+ *   cb, hsq, slot_mapping, index_cache, block_stride_bytes, first_block,
+ *   n_blocks      as for loopvq_encode.
+ * Requires dims->x_dtype == LOOPVQ_DTYPE_BF16 (else LOOPVQ_ERR_UNSUPPORTED).
+ */
+int loopvq_encode_pages(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
+                        int32_t n_blocks, const void* kv_pages, int64_t step_stride,
+                        const int32_t* src_slot, const void* cb, const float* hsq,
+                        const int32_t* slot_mapping, uint8_t* index_cache,
+                        int64_t block_stride_bytes, hipStream_t stream);
+
 /* Workspace bytes that loopvq_decode_attn and loopvq_decode_attn_window need
  * for this batch shape. */
 size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,

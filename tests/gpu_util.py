@@ -160,3 +160,24 @@ def make_cache_from_data(cfg, xk, xv, cb, lens, block_table, num_pages, method="
         ties += t
         off += int(n)
     return caches, ties
+
+
+def check_codes(cfg, got_cache, xk, xv, cb, slots, heads=None, blocks=None, method="gemm"):
+    """Compare GPU rows with the oracle's nearest entries; returns (near-tie count, mismatches)."""
+    P = cfg.page_size
+    heads = range(cfg.H_kv) if heads is None else heads
+    blocks = range(cfg.n_blocks) if blocks is None else blocks
+    ties = bad = 0
+    slots = np.asarray(slots, np.int64)
+    for beta in blocks:
+        for h in heads:
+            for kv, x in enumerate((xk, xv)):
+                rows = got_cache[beta][slots // P, h, kv, slots % P, :]
+                got = oracle.slots_to_groups(oracle.unpack_rows(rows, cfg.bits, cfg.n_groups)).reshape(-1)
+                z = oracle.coupled_vectors(x[:, :, h, :], cfg.Tc, cfg.c, beta).reshape(-1, cfg.G)
+                E = cb[beta, h, kv].astype(np.float64)
+                res = oracle.nearest_entry(z, E, method=method)
+                ties += int(res.near_tie.sum())
+                ok = oracle.accepts(z, E, res, got)
+                bad += int((~ok).sum())
+    return ties, bad

@@ -142,6 +142,24 @@ def test_encode_validation_before_launch(L):
     assert lib.loopvq_encode(ctypes.byref(d_small), 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
 
 
+def test_encode_pages_validation_before_launch(L):
+    lib = L.lib()
+    d = _dims(L)
+    def call(n_tok=10, first=0, nb=1, pages=FAKE, stride=1 << 20, src=FAKE, ptr=FAKE, dims=d):
+        return lib.loopvq_encode_pages(ctypes.byref(dims), n_tok, first, nb, pages, stride, src, ptr, ptr, ptr, ptr,
+                                       0, None)
+    assert call(pages=None) == -1
+    assert call(src=None) == -1
+    assert call(pages=ctypes.c_void_p((1 << 20) + 8)) == -1      # pool not 16-byte aligned
+    assert call(stride=0) == -1                                  # Tc = 4 steps need a step stride
+    assert call(stride=12) == -1                                 # stride not a multiple of 8
+    assert call(n_tok=-1) == -1
+    assert call(nb=2) == -1
+    assert call(ptr=None) == -1
+    assert call(dims=_dims(L, x_dtype="f32")) == -2              # the window pages are bf16
+    assert call(n_tok=0, pages=None, src=None) == 0
+
+
 def test_slices_validation(L):
     lib = L.lib()
     assert lib.loopvq_build_codebook_slices(ctypes.byref(_dims(L)), None, FAKE, None, None) == -1

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (GpuLayer, compare, dims_for, io_tensor, make_cache_from_data, ref_decode, to_dev,
-                      x_tensor)
+from gpu_util import (GpuLayer, check_codes, compare, dims_for, io_tensor, make_cache_from_data, ref_decode,
+                      to_dev, x_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,27 +35,6 @@ def _encode_gpu(cfg, layer, xk, xv, slots, num_pages, n_blocks=None, first_block
                      block_stride_bytes=cache[0].numel())
     torch.cuda.synchronize()
     return cache.cpu().numpy()
-
-
-def _check_codes(cfg, got_cache, xk, xv, cb, slots, heads=None, blocks=None, method="gemm"):
-    """Compare GPU rows with the oracle's nearest entries; returns (near-tie count, mismatches)."""
-    P = cfg.page_size
-    heads = range(cfg.H_kv) if heads is None else heads
-    blocks = range(cfg.n_blocks) if blocks is None else blocks
-    ties = bad = 0
-    slots = np.asarray(slots, np.int64)
-    for beta in blocks:
-        for h in heads:
-            for kv, x in enumerate((xk, xv)):
-                rows = got_cache[beta][slots // P, h, kv, slots % P, :]
-                got = oracle.slots_to_groups(oracle.unpack_rows(rows, cfg.bits, cfg.n_groups)).reshape(-1)
-                z = oracle.coupled_vectors(x[:, :, h, :], cfg.Tc, cfg.c, beta).reshape(-1, cfg.G)
-                E = cb[beta, h, kv].astype(np.float64)
-                res = oracle.nearest_entry(z, E, method=method)
-                ties += int(res.near_tie.sum())
-                ok = oracle.accepts(z, E, res, got)
-                bad += int((~ok).sum())
-    return ties, bad
 
 
 # ---------------------------------------------------------------- slices
@@ -86,7 +65,7 @@ def test_tiny_encode_and_decode():
     slots = synth.slot_mapping_for(bt, 0, N, cfg.page_size)
     layer = GpuLayer(cfg, cb, N)
     got = _encode_gpu(cfg, layer, xk, xv, slots, npg)
-    ties, bad = _check_codes(cfg, got, xk, xv, cb, slots, method="direct")
+    ties, bad = check_codes(cfg, got, xk, xv, cb, slots, method="direct")
     _note(f"tiny encode: near-ties {ties}, mismatches outside the band {bad}")
     assert bad == 0
     ref_cache, _, _ = oracle.build_index_cache(xk, xv, cb, cfg.Tc, cfg.c, cfg.bits, slots, npg, cfg.page_size)
@@ -117,7 +96,7 @@ def test_layer_ragged_encode_decode():
     slots = np.concatenate([synth.slot_mapping_for(bt, b, int(n), cfg.page_size) for b, n in enumerate(lens)])
     layer = GpuLayer(cfg, cb, int(lens.max()))
     got = _encode_gpu(cfg, layer, xk, xv, slots, npg)
-    ties, bad = _check_codes(cfg, got, xk, xv, cb, slots, heads=[0, 7, 15])
+    ties, bad = check_codes(cfg, got, xk, xv, cb, slots, heads=[0, 7, 15])
     _note(f"layer encode: near-ties {ties}, mismatches outside the band {bad}")
     assert bad == 0
     ref_cache, _ = make_cache_from_data(cfg, xk, xv, cb, lens, bt, npg)
@@ -193,7 +172,7 @@ def test_deep_loop_blocks():
     slots = synth.slot_mapping_for(bt, 0, n, cfg.page_size)
     layer = GpuLayer(cfg, cb, cfg.seq_len)
     got = _encode_gpu(cfg, layer, xk, xv, slots, npg)
-    ties, bad = _check_codes(cfg, got, xk, xv, cb, slots, heads=[0, 9])
+    ties, bad = check_codes(cfg, got, xk, xv, cb, slots, heads=[0, 9])
     _note(f"deeploop encode: near-ties {ties}, mismatches outside the band {bad}")
     assert bad == 0
     # decode at N = 16384, B = 4 from random caches of every block
@@ -267,7 +246,7 @@ def test_per_step_coding_runs_on_the_same_kernels():
     slots = synth.slot_mapping_for(bt, 0, n, cfg.page_size)
     layer = GpuLayer(cfg, cb, n)
     got = _encode_gpu(cfg, layer, xk, xv, slots, npg)
-    ties, bad = _check_codes(cfg, got, xk, xv, cb, slots)
+    ties, bad = check_codes(cfg, got, xk, xv, cb, slots)
     _note(f"per-step encode: near-ties {ties}, mismatches {bad}")
     assert bad == 0
     ref_cache, _ = make_cache_from_data(cfg, xk, xv, cb, lens, bt, npg)
