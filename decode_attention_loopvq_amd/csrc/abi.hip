@@ -60,7 +60,7 @@ DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   // duos of one chunk (pages of >= 16 positions, bf16 queries)
   pl.shared_rope = pl.n_dg % 8 == 0 && d->page_size >= 16 && d->io_dtype == LOOPVQ_DTYPE_BF16;
   const long long work = (long long)d->H_kv * pl.n_dg * len;
-  const long long step2 = (pl.shared_rope ? 6LL : 2LL) * pl.NT;   // steps per loop iteration
+  const long long step2 = (pl.shared_rope ? 4LL : 2LL) * pl.NT;   // steps per loop iteration
   // about 2048 waves (8 per CU) over the whole call
   long long Lc = (work + 2047) / 2048;
   Lc = (Lc + step2 - 1) / step2 * step2;

@@ -497,7 +497,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     int nst = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) nst = max(nst, wsteps[w]);
-    nst = (nst + 5) / 6 * 6;                 // six steps per iteration (ring x row buffers)
+    nst = (nst + 3) & ~3;                    // four steps per iteration (ring x row buffers)
     constexpr int PIECES = TSTEP / 16 / WAVES;   // 16-byte pieces per wave and step
     const int glast_st = (max(p.max_seq_len - 1, 0) >> 4) << 4;
     float4v sb[2];                           // staged pieces in flight
@@ -526,27 +526,31 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       for (int s = 0; s < NS; ++s)
         pg[s] = plist[s * PGMAX + min((min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
     };
-    uint32_t kw[3][NS][LW], vw[3][2][LW];
-    // one step: the rows of st+3 go to row buffer b3 = st % 3; staged pieces
-    // alternate with b2 = st % 2
-    // (scheduling fences keep the phases in this order, which bounds the
-    // live registers: the compiler would otherwise hoist loads and spill)
-    auto st_step = [&](int st, int b3, int b2) {
+    uint32_t kw[4][NS][LW], vw[4][2][LW];
+    int pgn[NS];                             // page ids of step st+3, read during step st-1
+    // one step: index rows of step x live in row buffer x % 4, staged pieces
+    // alternate with b2 = st % 2.  Every global load of a step (staged rows,
+    // index rows of st+3) and the page-id read are issued on every path and
+    // before the step's own work, so the number of operations younger than
+    // any awaited one is the same whether or not the wave still has steps:
+    // the wait counts stay loose (a wave waits for loads issued steps ago,
+    // never for the ones it has just issued).  Scheduling fences keep the
+    // phases in order, which bounds the live registers.
+    auto st_step = [&](int st, int b4, int b2) {
       wg_barrier();                                   // ring slot st&1 holds the rows of st
       stage_load(st + 2, sb[b2]);
+      row_load(st + 3, pgn, kw[(b4 + 3) & 3], vw[(b4 + 3) & 3]);
+      page_lds(st + 4, pgn);
       __builtin_amdgcn_sched_barrier(0);
       if (st < my_steps) {
         float sc[2], sv2[2];
-        int pg[NS];
-        page_lds(st + 3, pg);
         table_lds(st);
         k_side(sc);
         __builtin_amdgcn_sched_barrier(0);
-        gather_v(vw[b3]);                             // V entries of step st
-        row_load(st + 3, pg, kw[b3], vw[b3]);
+        gather_v(vw[b4]);                             // V entries of step st
         __builtin_amdgcn_sched_barrier(0);
         to_v_role(sc, sv2);
-        gather_k(kw[(b3 + 1) % 3]);                   // K entries of step st+1
+        gather_k(kw[(b4 + 1) & 3]);                   // K entries of step st+1
         __builtin_amdgcn_sched_barrier(0);
         v_side(p0 + st * NT, sv2);
         __builtin_amdgcn_sched_barrier(0);
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     if (nst > 0) {
       stage_load(0, sb[0]);
       stage_load(1, sb[1]);
-      if (my_steps > 0) {
+      {
         int pg[NS];
         page_lds(0, pg);
         row_load(0, pg, kw[0], vw[0]);
@@ -564,16 +568,15 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         row_load(1, pg, kw[1], vw[1]);
         page_lds(2, pg);
         row_load(2, pg, kw[2], vw[2]);
-        gather_k(kw[0]);
+        page_lds(3, pgn);
       }
+      if (my_steps > 0) gather_k(kw[0]);
       stage_store(0, sb[0]);
-      for (int st = 0; st < nst; st += 6) {
+      for (int st = 0; st < nst; st += 4) {
         st_step(st, 0, 0);
         st_step(st + 1, 1, 1);
         st_step(st + 2, 2, 0);
-        st_step(st + 3, 0, 1);
-        st_step(st + 4, 1, 0);
-        st_step(st + 5, 2, 1);
+        st_step(st + 3, 3, 1);
       }
     }
   }

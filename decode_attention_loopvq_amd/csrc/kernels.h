@@ -20,7 +20,7 @@ struct DecodeParams {
   int B, H_kv, H_q, grp, max_pages, log2P;
   int n_pairs;                // B * grp (request, query head) pairs per KV head
   int n_dg;                   // duos (pairs 2i, 2i+1) per KV head; one wave serves one duo
-  int Lc;                     // positions per chunk (one wave), a multiple of 32 (96 if shared_rope)
+  int Lc;                     // positions per chunk (one wave), a multiple of 32 (64 if shared_rope)
   int shared_rope;            // eight waves of a workgroup share a chunk and its RoPE rows
   int n_chunks;
   int items_per_head;         // n_dg * n_chunks wave work items per KV head
