@@ -151,13 +151,25 @@ def accepts(z: np.ndarray, E: np.ndarray, res: NearestResult, idx_other: np.ndar
 
 def encode_stream(x: np.ndarray, E: np.ndarray, Tc: int, c: int, beta: int,
                   method: str = "direct") -> tuple:
-    """Encode block `beta` of one cache stream x [T, N, D] with codebook E [K, c*Tc].
+    """Encode block `beta` of one cache stream x [T, N, D].
 
-    Returns (idx [N, D // c], NearestResult over the N*(D//c) coupled vectors).
+    E is either one codebook [K, c*Tc] shared by every channel group, or one
+    codebook per group [D // c, K, c*Tc] (P1 section "Loop-axis vector
+    quantization" writes the codebook of a code as B_{beta,l,h,g}: group g of
+    token j is then coded with E[g]).
+    Returns (idx [N, D // c], NearestResult over the N*(D//c) coupled vectors
+    in (token, group) order).
     """
     z = coupled_vectors(x, Tc, c, beta)
     N, ng, G = z.shape
-    res = nearest_entry(z.reshape(N * ng, G), E, method=method)
+    E = np.asarray(E)
+    if E.ndim == 2:
+        res = nearest_entry(z.reshape(N * ng, G), E, method=method)
+        return res.idx.reshape(N, ng), res
+    assert E.shape[0] == ng
+    parts = [nearest_entry(z[:, g, :], E[g], method=method) for g in range(ng)]
+    stack = lambda f: np.stack([getattr(r, f) for r in parts], axis=1).reshape(N * ng)
+    res = NearestResult(stack("idx"), stack("d1"), stack("d2"), stack("band"))
     return res.idx.reshape(N, ng), res
 
 
@@ -251,11 +263,20 @@ def loop_slice(E: np.ndarray, Tc: int, c: int, m: int) -> np.ndarray:
 
 
 def rebuild(idx: np.ndarray, E: np.ndarray, Tc: int, c: int, m: int) -> np.ndarray:
-    """Reconstruct one loop step: xhat[j, g*c + i] = e_{idx[j, g]}[i*Tc + m]."""
-    S = loop_slice(E, Tc, c, m)
+    """Reconstruct one loop step: xhat[j, g*c + i] = e_{idx[j, g]}[i*Tc + m].
+
+    E is a shared codebook [K, c*Tc] or one codebook per group [D // c, K, c*Tc]
+    (group g then reads entry idx[j, g] of E[g]).
+    """
     idx = np.asarray(idx, dtype=np.int64)
     N, ng = idx.shape
-    return S[idx].reshape(N, ng * c)
+    E = np.asarray(E)
+    if E.ndim == 2:
+        return loop_slice(E, Tc, c, m)[idx].reshape(N, ng * c)
+    out = np.empty((N, ng * c))
+    for g in range(ng):
+        out[:, g * c:(g + 1) * c] = loop_slice(E[g], Tc, c, m)[idx[:, g]]
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -317,7 +338,8 @@ def decode_attention(q: np.ndarray, cache_block: np.ndarray, block_table_row: np
 
     q: [H_q, D] queries (already rotated at their own position).
     cache_block: [num_pages, H_kv, 2, P, R] index cache of block (t-1)//Tc.
-    cb_block: [H_kv, 2, K, c*Tc] codebooks of that block.
+    cb_block: [H_kv, 2, K, c*Tc] codebooks of that block, or [H_kv, 2, D//c, K,
+    c*Tc] with one codebook per channel group.
     Query head j reads KV head j // (H_q / H_kv).
     Returns (o [H_q, D], lse [H_q]).
     """

@@ -418,3 +418,72 @@ def test_window_without_bf16_tokens_is_the_quantised_decode():
     o2, lse2 = oracle.decode_attention(q, cache, bt, N, cbb, 2, Tc, c, bits, 1e4)
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, lse2)
+
+
+# ---------------------------------------------------------------- one codebook per channel group
+def _pg_case(seed, H=2):
+    rng = np.random.default_rng(seed)
+    T, Tc, c, D, N, bits = 4, 4, 4, 32, 40, 8
+    ng = D // c
+    xk = rng.standard_normal((T, N, H, D))
+    xv = rng.standard_normal((T, N, H, D))
+    shared = rng.standard_normal((1, H, 2, 256, c * Tc)).astype(np.float16)
+    return rng, xk, xv, shared, T, Tc, c, D, N, bits, ng
+
+
+def test_per_group_codebooks_all_equal_reduce_to_the_shared_one():
+    rng, xk, xv, shared, T, Tc, c, D, N, bits, ng = _pg_case(21)
+    pg = np.broadcast_to(shared[:, :, :, None], (1, 2, 2, ng) + shared.shape[3:]).copy()
+    P = 8
+    bt = rng.permutation(N // P).astype(np.int32)[None, :]
+    slots = synth.slot_mapping_for(bt, 0, N, P)
+    a, _, _ = oracle.build_index_cache(xk, xv, shared, Tc, c, bits, slots, N // P, P)
+    b, _, _ = oracle.build_index_cache(xk, xv, pg, Tc, c, bits, slots, N // P, P)
+    np.testing.assert_array_equal(a, b)
+    q = rng.standard_normal((2, D))
+    o1, l1 = oracle.decode_attention(q, a[0], bt[0], N, shared[0], 2, Tc, c, bits, 1e4)
+    o2, l2 = oracle.decode_attention(q, b[0], bt[0], N, pg[0], 2, Tc, c, bits, 1e4)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_per_group_codebooks_follow_a_per_group_entry_permutation():
+    # group g's codebook is the shared one with its entries reordered by pi_g:
+    # every code becomes pi_g^-1 of the shared code, and the rebuilt data match
+    rng, xk, xv, shared, T, Tc, c, D, N, bits, ng = _pg_case(22, H=1)
+    perms = [rng.permutation(256) for _ in range(ng)]
+    pg = np.stack([shared[0, 0, 0][p] for p in perms])                       # [ng, K, G]
+    x = xk[:, :, 0, :]
+    i_sh, _ = oracle.encode_stream(x, shared[0, 0, 0], Tc, c, 0)
+    i_pg, _ = oracle.encode_stream(x, pg, Tc, c, 0)
+    for g in range(ng):
+        inv = np.argsort(perms[g])
+        np.testing.assert_array_equal(i_pg[:, g], inv[i_sh[:, g]])
+    for m in range(Tc):
+        np.testing.assert_array_equal(oracle.rebuild(i_pg, pg, Tc, c, m), oracle.rebuild(i_sh, shared[0, 0, 0], Tc, c, m))
+
+
+def test_per_group_lossless_codebooks_give_dense_attention():
+    # group g's codebook holds every coupled vector of group g: coding is
+    # lossless and decode equals attention over the rotated original keys
+    rng = np.random.default_rng(23)
+    T, Tc, c, D, N, bits, H = 4, 4, 4, 32, 40, 8, 1
+    ng = D // c
+    xk = rng.integers(-32, 32, size=(T, N, H, D)) / 8.0
+    xv = rng.integers(-32, 32, size=(T, N, H, D)) / 8.0
+    cb = np.zeros((1, H, 2, ng, 256, c * Tc), dtype=np.float16)
+    for kv, x in enumerate((xk, xv)):
+        z = oracle.coupled_vectors(x[:, :, 0, :], Tc, c, 0)                  # [N, ng, G]
+        for g in range(ng):
+            fill = 100.0 + np.arange(256 - N)[:, None] + rng.random((256 - N, c * Tc))
+            cb[0, 0, kv, g] = np.concatenate([z[:, g, :], fill]).astype(np.float16)
+    P = 8
+    bt = rng.permutation(N // P).astype(np.int32)[None, :]
+    slots = synth.slot_mapping_for(bt, 0, N, P)
+    caches, ties, _ = oracle.build_index_cache(xk, xv, cb, Tc, c, bits, slots, N // P, P)
+    assert ties == 0
+    for t in range(1, T + 1):
+        q = rng.standard_normal((1, D))
+        o, lse = oracle.decode_attention(q, caches[0], bt[0], N, cb[0], t, Tc, c, bits, 1e4)
+        krot = _rope_complex(xk[t - 1, :, 0, :], np.arange(N), 1e4)
+        np.testing.assert_allclose(o[0], _sdpa(q[0], krot, xv[t - 1, :, 0, :]), rtol=0, atol=1e-12)
