@@ -11,7 +11,8 @@ t = 1..4 from step to step.  The cache it reads was built beforehand by the
 GPU encoder from synthetic loop-correlated keys and values.  Two more legs
 are reported beside the headline: the same batch with a 64-token bf16 sink
 and a 256-token bf16 recent window ("window"), the decode-time coding of
-one 8-token window page per request ("page_encode"), and the encoder on the
+one 8-token window page per request ("page_encode"), the split pass with one
+codebook per channel group ("per_group"), and the encoder on the
 prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode").
 Prints one JSON line.
 """
@@ -200,6 +201,38 @@ def bench_window(args, torch, np, synth, lv, dec, n_sink=64, n_recent=256):
             "bf16_bytes_per_call": nbf * cfg.H_kv * 2 * cfg.D * 2}
 
 
+def bench_per_group(args, torch, np, synth, lv, dec):
+    """The split pass of the same 32K batch with one codebook per channel group:
+    the same index cache read through per-group slices."""
+    cfg, lens = dec["cfg"], dec["lens"]
+    B, max_seq_len = len(lens), dec["max_seq_len"]
+    dims = lv.loopvq_dims.make(D=cfg.D, c=cfg.c, Tc=cfg.Tc, T=cfg.T, bits=cfg.bits, H_kv=cfg.H_kv,
+                               H_q=cfg.H_q, page_size=cfg.page_size, x_dtype=cfg.x_dtype,
+                               io_dtype=cfg.io_dtype, per_group=1)
+    cb = torch.from_numpy(synth.make_codebooks_per_group(cfg)).cuda()
+    slices, _ = lv.loopvq_build_codebook_slices(dims, cb)
+    ws = torch.empty(lv.loopvq_decode_workspace_bytes(dims, B, max_seq_len), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        t = i % cfg.T + 1
+        lv.loopvq_decode_split(dims, t, dec["qs"][t - 1], dec["cache"][0], slices, dec["rope"], dec["bt"],
+                               dec["seq"], max_seq_len, ws, max_pos=max_seq_len)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "decode split with one codebook per channel group", "ms_per_call": round(ms, 5),
+            "value": round(float(lens.sum()) / (ms * 1e-3), 1), "unit": "cached tokens/s (split pass only)",
+            "workload": f"{cfg.name} batch, {cfg.n_groups} codebooks per (head, K|V): slices kept unreplicated "
+                        "in LDS"}
+
+
 def bench_page_encode(args, torch, np, synth, lv, dec):
     """Decode-time page encoding at the 32K batch's shape: the oldest 8-token bf16
     window page of each of the 16 requests, coded for all loop steps at once."""
@@ -330,6 +363,7 @@ def main():
     dec = bench_decode(args, torch, np, synth, lv)
     win = bench_window(args, torch, np, synth, lv, dec)
     penc = bench_page_encode(args, torch, np, synth, lv, dec)
+    pgr = bench_per_group(args, torch, np, synth, lv, dec)
     enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
     cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
     cfg = dec["cfg"]
@@ -358,6 +392,7 @@ def main():
         "per_loop_step_tokens_per_s": {k: round(v, 1) for k, v in dec["per_t_tokens_per_s"].items()},
         "window": win,
         "page_encode": penc,
+        "per_group": pgr,
         "encode": enc,
     }
     print(json.dumps(line), flush=True)

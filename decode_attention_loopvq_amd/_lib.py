@@ -28,13 +28,19 @@ class LoopVQError(RuntimeError):
 
 class loopvq_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("D", "c", "Tc", "T", "bits", "K", "H_kv", "H_q", "page_size", "x_dtype", "io_dtype")]
+                ("D", "c", "Tc", "T", "bits", "K", "H_kv", "H_q", "page_size", "x_dtype", "io_dtype",
+                 "per_group")]
 
     @classmethod
-    def make(cls, D, c, Tc, T, bits, H_kv, H_q, page_size, x_dtype="bf16", io_dtype="bf16"):
+    def make(cls, D, c, Tc, T, bits, H_kv, H_q, page_size, x_dtype="bf16", io_dtype="bf16", per_group=0):
         dt = {"f32": LOOPVQ_DTYPE_F32, "bf16": LOOPVQ_DTYPE_BF16}
         return cls(D, c, Tc, T, bits, 1 << bits, H_kv, H_q, page_size,
-                   dt.get(x_dtype, x_dtype), dt.get(io_dtype, io_dtype))
+                   dt.get(x_dtype, x_dtype), dt.get(io_dtype, io_dtype), int(per_group))
+
+    @property
+    def n_codebooks(self):
+        """Codebooks per (block, KV head, K|V): 1, or D/c with one per channel group."""
+        return self.D // self.c if self.per_group else 1
 
     @property
     def G(self):
@@ -141,12 +147,13 @@ def loopvq_row_bytes(dims: loopvq_dims) -> int:
 
 
 def loopvq_build_codebook_slices(dims: loopvq_dims, cb: torch.Tensor, slices=None, hsq=None):
-    """cb [n_blocks][H_kv][2][K][G] fp16 -> (slices [T][H_kv][2][K][c] fp16, hsq fp32)."""
+    """cb [n_blocks][H_kv][2]([D/c])[K][G] fp16 -> (slices [T][H_kv][2]([D/c])[K][c] fp16, hsq fp32)."""
     _need(cb, torch.float16, "cb")
+    ng = (dims.n_codebooks,) if dims.per_group else ()
     if slices is None:
-        slices = torch.empty((dims.T, dims.H_kv, 2, dims.K, dims.c), dtype=torch.float16, device=cb.device)
+        slices = torch.empty((dims.T, dims.H_kv, 2) + ng + (dims.K, dims.c), dtype=torch.float16, device=cb.device)
     if hsq is None:
-        hsq = torch.empty((dims.n_blocks, dims.H_kv, 2, dims.K), dtype=torch.float32, device=cb.device)
+        hsq = torch.empty((dims.n_blocks, dims.H_kv, 2) + ng + (dims.K,), dtype=torch.float32, device=cb.device)
     _check(lib().loopvq_build_codebook_slices(ctypes.byref(dims), _ptr(cb), _ptr(slices), _ptr(hsq),
                                               _stream()), "loopvq_build_codebook_slices")
     return slices, hsq

@@ -36,8 +36,13 @@ int check_dims(const loopvq_dims* d) {
   const int G = d->c * d->Tc;
   if (G != 8 && G != 16 && G != 32) return LOOPVQ_ERR_UNSUPPORTED;
   if (G == 8 && d->x_dtype != LOOPVQ_DTYPE_F32) return LOOPVQ_ERR_UNSUPPORTED;
+  if (d->per_group != 0 && d->per_group != 1) return LOOPVQ_ERR_INVALID_ARG;
+  if (d->per_group && d->bits != 8) return LOOPVQ_ERR_UNSUPPORTED;
   return LOOPVQ_OK;
 }
+
+// codebooks per (block, KV head, K|V): one, or one per channel group
+int n_codebook_groups(const loopvq_dims* d) { return d->per_group ? d->D / d->c : 1; }
 
 struct DecodePlan {
   int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid, shared_rope;
@@ -114,8 +119,11 @@ int loopvq_build_codebook_slices(const loopvq_dims* dims, const void* cb, void* 
   int st = check_dims(dims);
   if (st != LOOPVQ_OK) return st;
   if (cb == nullptr || slices == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  // one codebook per group: the groups' entries follow one another, so the
+  // slices are those of a codebook of n*K entries
   return hip_status(launch_build_slices((const uint16_t*)cb, (uint16_t*)slices, hsq, dims->T / dims->Tc,
-                                        dims->H_kv, dims->K, dims->c, dims->Tc, stream));
+                                        dims->H_kv, dims->K * n_codebook_groups(dims), dims->c, dims->Tc,
+                                        stream));
 }
 
 int loopvq_rope_table(int32_t max_pos, int32_t D, double base, float* table) {
@@ -161,7 +169,7 @@ static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   if ((dims->D / dims->c) % 16 != 0) return LOOPVQ_ERR_UNSUPPORTED;
   if (n_tok == 0) return LOOPVQ_OK;
   if (!xk || !xv || !cb || !hsq || !slot_mapping || !index_cache) return LOOPVQ_ERR_INVALID_ARG;
-  const int H = dims->H_kv, K = dims->K, G = dims->c * dims->Tc;
+  const int H = dims->H_kv, K = dims->K * n_codebook_groups(dims), G = dims->c * dims->Tc;
   EncodeParams p{};
   p.xk = xk;
   p.xv = xv;
@@ -177,11 +185,14 @@ static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   p.D = dims->D;
   p.c = dims->c;
   p.Tc = dims->Tc;
-  p.K = K;
+  p.K = dims->K;
   p.log2P = ilog2(dims->page_size);
-  // units of 32 (token, group) vectors; about 8192 waves over the whole call
-  const long long streams = (long long)n_blocks * 2 * H;
-  const long long units = ((long long)n_tok * (dims->D / dims->c) + 31) / 32;
+  p.per_group = dims->per_group;
+  // units of 32 (token, group) vectors (per group: 32 tokens of one group);
+  // about 8192 waves over the whole call
+  const long long streams = (long long)n_blocks * 2 * H * n_codebook_groups(dims);
+  const long long units = dims->per_group ? ((long long)n_tok + 31) / 32
+                                          : ((long long)n_tok * (dims->D / dims->c) + 31) / 32;
   long long upw = (streams * units + 8191) / 8192;
   upw = std::max<long long>(1, std::min<long long>(upw, units));
   p.units_per_wave = (int)upw;
@@ -256,7 +267,7 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
   DecodeParams p{};
   p.q = q;
   p.cache = index_cache;
-  p.slices = (const uint16_t*)slices + (size_t)(t - 1) * dims->H_kv * 2 * dims->K * dims->c;
+  p.slices = (const uint16_t*)slices + (size_t)(t - 1) * dims->H_kv * 2 * dims->K * n_codebook_groups(dims) * dims->c;
   p.rope = rope_table;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
@@ -279,8 +290,9 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
   p.max_seq_len = max_seq_len;
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)dims->D);
   p.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(launch_decode_split(dims->D, dims->c, dims->bits, dims->io_dtype == LOOPVQ_DTYPE_F32, p,
-                                        pl.grid, stream));
+  const bool qf32 = dims->io_dtype == LOOPVQ_DTYPE_F32;
+  if (dims->per_group) return hip_status(launch_decode_split_pg(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
+  return hip_status(launch_decode_split(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
 }
 
 // the combine pass; win_o / win_lse: the bf16-token partials, or null

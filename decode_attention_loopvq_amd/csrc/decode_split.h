@@ -1,0 +1,697 @@
+// Quantised split-K decode attention for LoopVQ on gfx950.
+//
+// What it computes [LoopVQ paper, hub.valency.io/works/W_7srt5hed_v1,
+// section "System implementation", attention; appendix
+// "Optimizing pre-RoPE vector quantization serving efficiency"]: at loop step t every
+// cached token j of a request contributes its key rebuilt from the step's
+// codebook slice, rotated by RoPE at position j, and its value rebuilt the
+// same way; tokens are cut into splits whose partial softmax outputs are
+// merged by their logsumexp (the combine kernel), which recovers the exact
+// softmax over all tokens.
+//
+// MI355X mapping (this file's own design, not the pages'):
+//  * A workgroup is eight waves on one KV head.  The head's K and V slices are
+//    staged once in LDS, every entry replicated over a 256-byte row (one copy
+//    per bank window), and lane l reads window l mod (256 / entry bytes):
+//    random code gathers of a wave then hit each of the 64 banks once per
+//    pass.  A gather address is one v_perm_b32 (code -> byte 1, lane window
+//    -> byte 0, K|V region -> byte 2).
+//  * A wave serves a duo of (request, query head) pairs 2i and 2i+1 over a
+//    chunk of positions, 16 positions per step.  When the GQA group is even
+//    the duo's pairs are query heads of one request and share one index
+//    stream and its key gathers.
+//  * K side: a lane owns one position (of its 16-lane row) and one quarter
+//    of the RoPE frequencies.  For each frequency one v_mfma_f32_4x4x4f16 with
+//    the block-diagonal query matrix [[q0_f, q0_h], [q0_h, -q0_f]] (+) the same
+//    for pair 1 and the key column (k0_f, k0_h, k1_f, k1_h) yields
+//    X = q_f k_f + q_h k_h and Y = q_h k_f - q_f k_h of both pairs with exact
+//    fp16 products; the lane then adds cos*X + sin*Y in fp32, which equals
+//    q . RoPE(k).  One load of cos/sin serves both pairs.
+//  * V side: rows 0-1 of the wave serve pair 0, rows 2-3 pair 1; a lane takes
+//    two positions and one channel quarter, and the same MFMA with A = p*I
+//    and the gathered V entries as B accumulates p*v in fp32 registers.
+//  * Online softmax in the log2 domain with a lazy maximum: the running max
+//    is only raised when a score exceeds it by more than 8 (so p <= 256).
+//  * RoPE rows come from a table interleaved by groups of 4 positions (one
+//    contiguous 256-byte run per 16 lanes); with eight duos per head the
+//    workgroup stages each step's rows once into an LDS ring (see below).
+#pragma once
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace loopvq {
+
+constexpr float LAZY_TAU = 8.0f;
+
+template <int LB>
+struct RowLoad;
+template <> struct RowLoad<1> { static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* w) { w[0] = *p; } };
+template <> struct RowLoad<2> { static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* w) { w[0] = *(const uint16_t*)p; } };
+template <> struct RowLoad<4> { static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* w) { w[0] = *(const uint32_t*)p; } };
+template <> struct RowLoad<8> { static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* w) {
+  uint2v v = *(const uint2v*)p; w[0] = v.x; w[1] = v.y; } };
+template <> struct RowLoad<16> { static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* w) {
+  uint4v v = *(const uint4v*)p; w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; } };
+
+// LDS address of the entry whose code sits in slot s of the lane's row words
+template <int BITS>
+__device__ __forceinline__ uint32_t slot_addr(const uint32_t* w, int s, uint32_t lane_off) {
+  if constexpr (BITS == 8) {
+    // byte 1 <- code; bytes 0 and 2 <- lane offset (window, K|V region); byte 3 <- 0
+    return perm(w[s >> 2], lane_off, 0x0c020000u | ((4u + (s & 3)) << 8));
+  } else {
+    uint32_t code = (w[s >> 3] >> ((s & 7) * 4)) & 15u;
+    return (code << 8) | lane_off;
+  }
+}
+
+// one codebook per channel group: LDS address of the entry whose code sits in
+// slot s of the lane's row words.  The lane's quarter is folded into base; slot
+// s < Q is group base_group + s, slot Q + r its RoPE partner N/2 + base_group + r,
+// and entry e of group g sits at (g*KENT + e)*EB (no replication)
+template <int BITS, int EB, int KENT, int Q, int N>
+__device__ __forceinline__ uint32_t slot_addr_pg(const uint32_t* w, int s, uint32_t base) {
+  uint32_t code;
+  if constexpr (BITS == 8) code = (w[s >> 2] >> ((s & 3) * 8)) & 255u;
+  else code = (w[s >> 3] >> ((s & 7) * 4)) & 15u;
+  const int gc = s < Q ? s : N / 2 + s - Q;
+  return code * EB + base + (uint32_t)(gc * KENT * EB);
+}
+
+template <int EB>
+struct Entry { uint32_t d[EB / 4]; };
+
+template <int EB>
+__device__ __forceinline__ Entry<EB> lds_entry(const uint8_t* lds, uint32_t addr) {
+  Entry<EB> e;
+  if constexpr (EB == 4) {
+    e.d[0] = *(const uint32_t*)(lds + addr);
+  } else if constexpr (EB == 8) {
+    uint2v v = *(const uint2v*)(lds + addr); e.d[0] = v.x; e.d[1] = v.y;
+  } else {
+    uint4v v = *(const uint4v*)(lds + addr); e.d[0] = v.x; e.d[1] = v.y; e.d[2] = v.z; e.d[3] = v.w;
+  }
+  return e;
+}
+
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP, bool ST, bool PG>
+__global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
+  constexpr int N = D / C;            // groups per row
+  constexpr int Q = N / 8;            // lo (and hi) groups per lane quarter
+  constexpr int F = D / 8;            // RoPE frequencies per lane quarter (one K MFMA each)
+  constexpr int FP = F / 2;           // float4 table words per quarter (two frequencies each)
+  constexpr int EB = 2 * C;           // bytes of one slice entry
+  constexpr int NWIN = 256 / EB;      // bank windows per 256-byte LDS row (64 banks)
+  constexpr int R = N * BITS / 8;     // row bytes
+  constexpr int LB = R / 4;           // row bytes per lane quarter
+  constexpr int LW = (LB + 3) / 4;    // row words per lane
+  constexpr int U = D / 16;           // 4-channel V units per lane and pair
+  constexpr int KENT = 1 << BITS;
+  constexpr int NS = SHARE ? 1 : 2;   // index streams per wave: the duo's requests
+  constexpr int NT = 16;              // positions per wave step
+  constexpr int SW = 4 * U + 3;       // floats of one lane's softmax state (one pair)
+  constexpr int WAVES = 8;            // waves per workgroup, all on one KV head
+  constexpr int TSTEP = NT * D * 4;   // bytes of the RoPE rows of one step
+  // slices: shared codebook, every entry replicated over a 256-byte row;
+  // one codebook per group (PG), the N*KENT entries of each of K and V packed
+  constexpr int LDS_SLICES = PG ? 2 * N * KENT * EB : 2 * KENT * 256;
+  constexpr int LDS_RING = ST ? 2 * TSTEP : 0;
+  constexpr int PGMAX = 128;          // page-list entries per stream and wave (shared rows)
+  constexpr int LDS_PAGES = ST ? WAVES * 2 * PGMAX * 4 : 0;
+  constexpr int LDS_MERGE = WAVES * 64 * SW * 4;
+  constexpr int LDS_BYTES = LDS_SLICES + LDS_RING + LDS_PAGES > LDS_MERGE ? LDS_SLICES + LDS_RING + LDS_PAGES
+                                                                          : LDS_MERGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ int wsteps[WAVES];
+
+  // ---- workgroup -> (KV head, 8 work items).  Heads vary fastest, so each
+  //      XCD (blocks of one residue mod 8, renumbered contiguously) owns a
+  //      band of chunks of every head: its L2 holds only that band's RoPE rows.
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int wgi = bid / p.H_kv;
+  const int h = bid - wgi * p.H_kv;
+
+  // ---- stage the K and V slices of head h, each entry replicated over a
+  //      256-byte row (one copy per bank window): entry e of region kv sits
+  //      at kv*KENT*256 + e*256, and lane l reads window l % NWIN, so the
+  //      random gathers of a wave hit every bank once per pass
+  if constexpr (PG) {
+    // one codebook per channel group: the head's [2][N][KENT] entries as they
+    // are (random gathers then meet bank conflicts; 256-byte replication of
+    // N*KENT entries would not fit in LDS)
+    const uint4v* src = (const uint4v*)((const uint8_t*)p.slices + (size_t)h * LDS_SLICES);
+    for (int x = threadIdx.x; x < LDS_SLICES / 16; x += blockDim.x) ((uint4v*)lds)[x] = src[x];
+  } else {
+    const uint8_t* src = (const uint8_t*)p.slices + (size_t)h * 2 * KENT * EB;
+    for (int x = threadIdx.x; x < 2 * KENT * 16; x += blockDim.x) {
+      const int ke = x >> 4, cchunk = x & 15;           // ke = kv * KENT + e
+      const uint8_t* sp = src + (size_t)ke * EB;
+      uint4v v;
+      if constexpr (EB == 16) {
+        v = *(const uint4v*)sp;
+      } else if constexpr (EB == 8) {
+        uint2v t = *(const uint2v*)sp; v = (uint4v){t.x, t.y, t.x, t.y};
+      } else {
+        uint32_t t = *(const uint32_t*)sp; v = (uint4v){t, t, t, t};
+      }
+      *(uint4v*)(lds + ke * 256 + cchunk * 16) = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- this wave's work item (wave-uniform): one duo of pairs, one chunk
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int item = wgi * WAVES + wave;
+  const bool item_ok = item < p.items_per_head;
+  const int ch = item_ok ? item / p.n_dg : 0;
+  const int duo = item_ok ? item - ch * p.n_dg : 0;
+  const int row = lane >> 4;                 // position group of this 16-lane row
+  const int la = (lane >> 2) & 3, lb = lane & 3;
+  // K role: quarter la, position slot lb.  V role: position slot la, quarter lb.
+  // coded positions of stream s: [lo[s], len[s]) (positions below lo[s] are
+  // a bf16 sink attended elsewhere); has[s]: the stream has coded positions
+  int kq[2], bq[2], len[2], lo[2];
+  bool okq[2], has[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    kq[s] = 2 * duo + s;
+    okq[s] = item_ok && kq[s] < p.n_pairs;
+    bq[s] = okq[s] ? kq[s] / p.grp : 0;
+    len[s] = okq[s] ? min(max(p.seq_lens[bq[s]], 0), p.max_seq_len) : 0;
+    lo[s] = (okq[s] && p.seq_lo != nullptr) ? min(max(p.seq_lo[bq[s]], 0), len[s]) : 0;
+    has[s] = lo[s] < len[s];
+  }
+  const int p0 = ch * p.Lc;
+  const int lenx = max(len[0], len[1]);
+  const bool active = item_ok && p0 < lenx;   // wave-uniform
+
+  // V role: rows 0-1 of the wave serve pair 0 and rows 2-3 pair 1; a lane
+  // takes position slot la of the step's groups 2*rp and 2*rp + 1 (positions
+  // 8*rp + la and 8*rp + 4 + la) and channel quarter lb
+  const int sv = row >> 1, rp = row & 1;
+  float m = -INFINITY;                   // running max (log2 domain)
+  float l = 0.f;                         // sum of the rounded p used in the products
+  float lx = 0.f;                        // exact sum of p (for the logsumexp)
+  float4v acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  // ---- K-side A operands (read by active waves only).  For frequency f (the
+  //      i-th of quarter la) lane lb supplies row lb of the block-diagonal
+  //        [[q0_f, q0_h, 0, 0], [q0_h, -q0_f, 0, 0], [0, 0, q1_f, q1_h], [0, 0, q1_h, -q1_f]]
+  //      (q_h = q_{f + D/2}; pair 0 and pair 1 of the duo), so that with the
+  //      key column (k0_f, k0_h, k1_f, k1_h) of a position the MFMA yields
+  //      X0, Y0, X1, Y1 of that position.
+  half4v AK[F];
+  half4v AKl[QF32 ? F : 1];
+  if (active) {
+    const int s = lb >> 1;
+    const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
+    const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
+    const size_t qoff = ((size_t)bb * p.H_q + jq) * D + la * F;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      float a, c;
+      if constexpr (QF32) {
+        a = ((const float*)p.q)[qoff + i];
+        c = ((const float*)p.q)[qoff + D / 2 + i];
+      } else {
+        a = u2f((uint32_t)((const uint16_t*)p.q)[qoff + i] << 16);
+        c = u2f((uint32_t)((const uint16_t*)p.q)[qoff + D / 2 + i] << 16);
+      }
+      const float x0 = (lb & 1) ? c : a, x1 = (lb & 1) ? -a : c;
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 z = (_Float16)0.f;
+      AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
+      if constexpr (QF32) {
+        const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+        AKl[i] = s ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
+      }
+    }
+  }
+
+  // ---- lane constants
+  // K window / V window in LDS (PG: the lane quarter's first group of K / V)
+  const uint32_t koff = PG ? (uint32_t)(la * Q * KENT * EB) : (uint32_t)(lane % NWIN) * EB;
+  const uint32_t voff = PG ? (uint32_t)((N + lb * Q) * KENT * EB) : (uint32_t)(KENT * 256) + koff;
+  const uint32_t asel0 = lb == 0 ? 0x0c0c0100u : (lb == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
+  const uint32_t asel1 = lb == 2 ? 0x0c0c0100u : (lb == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
+  // K-role lanes holding my V positions: row 2*rp (+1), position slot la;
+  // quarters 2*sv, 2*sv + 1 expose pair sv's score after the quarter sum
+  const int bperm_a = ((32 * rp) | ((2 * sv + (lb & 1)) << 2) | la) << 2;
+  const int bperm_b = bperm_a + 64;
+  const int P = 1 << p.log2P;
+  const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
+  const size_t page_stride = (size_t)p.H_kv * 2 * kv_stride;
+  const uint8_t* head_base = p.cache + (size_t)h * 2 * kv_stride;
+  // byte offsets of the lane's K and V row quarters from the first row of
+  // its group: the whole step inside one page (SP), or the row's own 4
+  // positions (pages of 8 positions)
+  const uint32_t kro = (uint32_t)(((SP ? 4 * row : 0) + lb) * R + la * LB);
+  const uint32_t vro = kv_stride + (uint32_t)(((SP ? 8 * rp : 0) + la) * R + lb * LB);   // +4R: slot b
+  const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
+  int lim[2], last[2];
+  const int32_t* btb[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    lim[s] = min(len[s], p0 + p.Lc);
+    last[s] = max(len[s] - 1, 0);
+    btb[s] = p.block_table + (size_t)bq[s] * p.max_pages;
+  }
+  const int limx = max(lim[0], lim[1]);
+  // the V lane's positions 8*rp + la (+4) of a step, relative to lo, and the
+  // span [lo, lim) of coded positions in this chunk
+  const int vrel = 8 * rp + la - lo[sv];
+  const uint32_t vspan = (uint32_t)max(lim[sv] - lo[sv], 0);
+  const int glast = (max(last[0], last[1]) >> 4) << 4;   // last step-aligned group with data
+  const int my_steps = active ? (limx - p0 + NT - 1) / NT : 0;   // wave-uniform
+  // an opaque zero: keeps the page-id loads on the vector path, in order
+  // with the row loads (scalar loads would share a counter with the LDS gathers)
+  const int vz = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
+
+  // raw block-table entries of the step's pages (only trusted when the
+  // stream's length is positive): one per stream with whole-step pages (SP);
+  // else per lane, one per stream for the K row group and one for the V groups
+  constexpr int NPG = SP ? NS : NS + 1;
+  auto page_at = [&](int st, int* pg) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (SP) pg[s] = btb[s][(min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) + vz];
+      else pg[s] = btb[s][min(max(p0 + st * NT + 4 * row, lo[s]), last[s]) >> p.log2P];
+    }
+    if constexpr (!SP) pg[NS] = btb[sv][min(max(p0 + st * NT + 8 * rp, lo[sv]), last[sv]) >> p.log2P];
+  };
+  // K rows of both streams at the lane's K position, V rows of stream sv at
+  // the lane's two V positions
+  auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW]) {
+    const uint8_t* vbase;
+    if constexpr (SP) {
+      const uint8_t* base[2];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int page = has[s] ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
+        const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
+        base[s] = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+        RowLoad<LB>::load(base[s] + kro, kw[s]);
+      }
+      vbase = (NS == 1 || sv == 0) ? base[0] : base[NS - 1];
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int page = has[s] ? raw_page[s] : 0;
+        const int gs = min(p0 + st * NT + 4 * row, last[s]) & ~3;
+        RowLoad<LB>::load(head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R + kro, kw[s]);
+      }
+      const int page = has[sv] ? raw_page[NS] : 0;
+      const int gs = min(p0 + st * NT + 8 * rp, last[sv]) & ~7;
+      vbase = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+    }
+    RowLoad<LB>::load(vbase + vro, vw[0]);
+    RowLoad<LB>::load(vbase + vro + 4 * R, vw[1]);
+  };
+  // table rows of positions 4g..4g+3 are interleaved: chunk j of quarter la
+  // of position 4g + n sits at float4 ((g*FP + j)*4 + la)*4 + n, so the 16
+  // lanes of a row (4 positions x 4 quarters) read one contiguous 256-B run,
+  // and the rows of one step form one contiguous TSTEP-byte block
+  float4v tb[FP];
+  auto table_load = [&](int st) {
+    const int gt = min(p0 + st * NT, glast);
+    const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
+#pragma unroll
+    for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
+  };
+
+  auto entry_addr = [&](const uint32_t* w, int s, uint32_t off) {
+    if constexpr (PG) return slot_addr_pg<BITS, EB, KENT, Q, N>(w, s, off);
+    else return slot_addr<BITS>(w, s, off);
+  };
+  // gathered K slice entries per stream, V entries per V position slot
+  Entry<EB> klo[NS][Q], khi[NS][Q], ve[2][2 * Q];
+  auto gather_k = [&](uint32_t (*kw)[LW]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int r = 0; r < Q; ++r) {
+        klo[s][r] = lds_entry<EB>(lds, entry_addr(kw[s], r, koff));
+        khi[s][r] = lds_entry<EB>(lds, entry_addr(kw[s], Q + r, koff));
+      }
+  };
+  auto gather_v = [&](uint32_t (*vw)[LW]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int sl = 0; sl < 2 * Q; ++sl) ve[t][sl] = lds_entry<EB>(lds, entry_addr(vw[t], sl, voff));
+  };
+
+  // ---- K side of a step: X, Y of both pairs for every frequency on the
+  //      matrix cores, then s = sum_f cos_f X_f + sin_f Y_f in fp32 (this
+  //      lane's quarter; klo/khi and tb hold the step's entries and rows)
+  auto k_side = [&](float* sc) {
+    float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      const int r = i / C, e = i % C;                      // entry and element of frequency i
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
+      const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
+      const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
+      float4v xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
+      const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
+      const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
+      sa0 = fmaf(cs, xy.x, sa0);
+      sb0 = fmaf(sn, xy.y, sb0);
+      sa1 = fmaf(cs, xy.z, sa1);
+      sb1 = fmaf(sn, xy.w, sb1);
+    }
+    // interleave: each MFMA is followed by VALU work (the next perms and this
+    // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QF32 ? 2 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    sc[0] = sa0 + sb0;
+    sc[1] = sa1 + sb1;
+  };
+  // sum over the four quarters (lanes 4 apart within the 16-lane row); lanes
+  // of quarters 0-1 then expose pair 0's score and quarters 2-3 pair 1's, and
+  // each V lane pulls its two positions of its pair
+  auto to_v_role = [&](const float* sc, float* sv2) {
+    float v0 = sc[0], v1 = sc[1];
+    v0 += u2f(__builtin_amdgcn_mov_dpp(f2u(v0), 0x124, 0xf, 0xf, true));   // row_ror:4
+    v1 += u2f(__builtin_amdgcn_mov_dpp(f2u(v1), 0x124, 0xf, 0xf, true));
+    v0 += u2f(__builtin_amdgcn_mov_dpp(f2u(v0), 0x128, 0xf, 0xf, true));   // row_ror:8
+    v1 += u2f(__builtin_amdgcn_mov_dpp(f2u(v1), 0x128, 0xf, 0xf, true));
+    const uint32_t ex = f2u(la >= 2 ? v1 : v0);
+    sv2[0] = u2f(__builtin_amdgcn_ds_bpermute(bperm_a, ex));
+    sv2[1] = u2f(__builtin_amdgcn_ds_bpermute(bperm_b, ex));
+  };
+  // ---- online softmax of pair sv at the lane's two positions (log2 domain,
+  //      lazy max) and the V side: acc += p * v on the matrix cores (block =
+  //      one token); p is rounded to fp16 for the product, and l adds the same
+  //      rounded p, so the output stays an exact convex combination
+  auto v_side = [&](int g0, const float* sv2) {
+    const int posa = g0 + vrel;
+    const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 4) < vspan;
+    const float sa = va ? sv2[0] * p.scale_log2 : -INFINITY;
+    const float sb = vb ? sv2[1] * p.scale_log2 : -INFINITY;
+    const float smax = fmaxf(sa, sb);
+    const bool need = smax > m + LAZY_TAU;
+    if (__ballot(need) != 0) {
+      if (need) {
+        const float fct = __builtin_amdgcn_exp2f(m - smax);
+        l *= fct;
+        lx *= fct;
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] *= fct;
+        m = smax;
+      }
+    }
+    const float pa = va ? __builtin_amdgcn_exp2f(sa - m) : 0.f;
+    const float pb = vb ? __builtin_amdgcn_exp2f(sb - m) : 0.f;
+    lx += pa + pb;
+    half4v A[2], Alo[2];
+    const float pv[2] = {pa, pb};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const _Float16 ph = (_Float16)pv[t];
+      const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
+      A[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
+      // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
+      if constexpr (QF32) {
+        const _Float16 pl = (_Float16)(pv[t] - (float)ph);
+        const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
+        Alo[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
+        l += (float)ph + (float)pl;
+      } else {
+        l += (float)ph;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int sl = 0; sl < 2 * Q; ++sl) {
+        if constexpr (EB == 8) {
+          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
+          acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, acc[sl], 0, 0, 0);
+          if constexpr (QF32) acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, acc[sl], 0, 0, 0);
+        } else if constexpr (EB == 16) {
+          const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
+          const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[2], ve[t][sl].d[3]});
+          acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B0, acc[2 * sl], 0, 0, 0);
+          if constexpr (QF32) acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B0, acc[2 * sl], 0, 0, 0);
+          acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B1, acc[2 * sl + 1], 0, 0, 0);
+          if constexpr (QF32) acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B1, acc[2 * sl + 1], 0, 0, 0);
+        } else if (sl & 1) {
+          // two 2-channel entries form one 4-channel unit
+          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl - 1].d[0], ve[t][sl].d[0]});
+          acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, acc[sl >> 1], 0, 0, 0);
+          if constexpr (QF32) acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, acc[sl >> 1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if constexpr (!ST) {
+    // ================= per-wave RoPE rows (any batch shape)
+    if (active) {
+      const int steps = (my_steps + 1) & ~1;   // two steps per iteration
+      // one decode step.  On entry klo/khi/ve hold the gathers of step st, tb
+      // the RoPE rows of st, and (kwn, vwn) the index rows of step st+1.  The
+      // step reloads tb for st+1 and gathers step st+1 as soon as the
+      // registers free up, then refills (kwn, vwn) with the rows of st+3
+      // (page ids pgr, read two steps earlier) and reads the pages of st+5.
+      auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], int* pgr) {
+        float sc[2], sv2[2];
+        k_side(sc);
+        table_load(st + 1);                             // RoPE rows of step st+1
+        to_v_role(sc, sv2);
+        gather_k(kwn);                                  // K entries of step st+1
+        v_side(p0 + st * NT, sv2);
+        gather_v(vwn);                                  // V entries of step st+1
+        row_load(st + 3, pgr, kwn, vwn);
+        page_at(st + 5, pgr);
+      };
+      uint32_t kwA[NS][LW], vwA[2][LW], kwB[NS][LW], vwB[2][LW];
+      int pgA[NPG], pgB[NPG], pg0[NPG];
+      page_at(0, pg0);
+      row_load(0, pg0, kwA, vwA);
+      page_at(1, pg0);
+      row_load(1, pg0, kwB, vwB);
+      table_load(0);
+      gather_k(kwA);
+      gather_v(vwA);
+      page_at(2, pg0);
+      row_load(2, pg0, kwA, vwA);
+      page_at(3, pgB);
+      page_at(4, pgA);
+      // an active wave has steps >= 2; the first two steps are peeled so that
+      // the loads outstanding at the loop head are in the same order on entry
+      // and on the back edge (the wait counts at the head are then tight)
+      do_step(0, kwB, vwB, pgB);
+      do_step(1, kwA, vwA, pgA);
+      for (int st = 2; st < steps; st += 2) {
+        do_step(st, kwB, vwB, pgB);
+        do_step(st + 1, kwA, vwA, pgA);
+      }
+    }
+  } else {
+    // ================= RoPE rows shared by the workgroup.  The eight waves
+    // work on one chunk (eight duos of one head), so each step's TSTEP bytes
+    // of rows are fetched once per workgroup, one 16-byte piece per lane of
+    // each wave, into a two-slot LDS ring, and read back by every wave.  The
+    // workgroup moves in lockstep (one barrier per step); waves whose duo has
+    // fewer steps keep staging rows for the others.
+    // the chunk's block-table entries of each stream, copied once into LDS
+    // (read back per step with no long-lived registers): entry i of stream s
+    // is the page of index pa[s] + i
+    int* plist = (int*)(lds + LDS_SLICES + LDS_RING) + wave * 2 * PGMAX;
+    int pa[2], pcnt[2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      pa[s] = min(max(p0, lo[s]), last[s]) >> p.log2P;
+      pcnt[s] = max(min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX), 1);
+      for (int i = lane; i < pcnt[s]; i += 64) plist[s * PGMAX + i] = has[s] ? btb[s][pa[s] + i] : 0;
+    }
+    if (lane == 0) wsteps[wave] = my_steps;
+    __syncthreads();
+    int nst = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) nst = max(nst, wsteps[w]);
+    nst = (nst + 3) & ~3;                    // four steps per iteration (ring x row buffers)
+    constexpr int PIECES = TSTEP / 16 / WAVES;   // 16-byte pieces per wave and step
+    const int glast_st = (max(p.max_seq_len - 1, 0) >> 4) << 4;
+    float4v sb[2];                           // staged pieces in flight
+    auto stage_load = [&](int st, float4v& dst) {
+      const int gt = min(p0 + st * NT, glast_st);
+      if (lane < PIECES) dst = ((const float4v*)p.rope)[(size_t)(gt >> 2) * FP * 16 + wave * PIECES + lane];
+    };
+    auto stage_store = [&](int st, const float4v& v) {
+      if (lane < PIECES) *(float4v*)(lds + LDS_SLICES + (st & 1) * TSTEP + (wave * PIECES + lane) * 16) = v;
+    };
+    auto table_lds = [&](int st) {
+      const uint8_t* ring = lds + LDS_SLICES + (st & 1) * TSTEP + tbo;
+#pragma unroll
+      for (int j = 0; j < FP; ++j) tb[j] = *(const float4v*)(ring + j * 256);
+    };
+    // this wave's LDS writes are done, then the workgroup meets
+    auto wg_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0), other counters untouched
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ __volatile__("" ::: "memory");
+    };
+    // page ids of step st (uniform values, clamped into the chunk's list)
+    auto page_lds = [&](int st, int* pg) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        pg[s] = plist[s * PGMAX + min((min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
+    };
+    uint32_t kw[4][NS][LW], vw[4][2][LW];
+    int pgn[NS];                             // page ids of step st+3, read during step st-1
+    // one step: index rows of step x live in row buffer x % 4, staged pieces
+    // alternate with b2 = st % 2.  Every global load of a step (staged rows,
+    // index rows of st+3) and the page-id read are issued on every path and
+    // before the step's own work, so the number of operations younger than
+    // any awaited one is the same whether or not the wave still has steps:
+    // the wait counts stay loose (a wave waits for loads issued steps ago,
+    // never for the ones it has just issued).  Scheduling fences keep the
+    // phases in order, which bounds the live registers.
+    auto st_step = [&](int st, int b4, int b2) {
+      wg_barrier();                                   // ring slot st&1 holds the rows of st
+      stage_load(st + 2, sb[b2]);
+      row_load(st + 3, pgn, kw[(b4 + 3) & 3], vw[(b4 + 3) & 3]);
+      page_lds(st + 4, pgn);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < my_steps) {
+        float sc[2], sv2[2];
+        table_lds(st);
+        k_side(sc);
+        __builtin_amdgcn_sched_barrier(0);
+        gather_v(vw[b4]);                             // V entries of step st
+        __builtin_amdgcn_sched_barrier(0);
+        to_v_role(sc, sv2);
+        gather_k(kw[(b4 + 1) & 3]);                   // K entries of step st+1
+        __builtin_amdgcn_sched_barrier(0);
+        v_side(p0 + st * NT, sv2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stage_store(st + 1, sb[1 - b2]);
+    };
+    if (nst > 0) {
+      stage_load(0, sb[0]);
+      stage_load(1, sb[1]);
+      {
+        int pg[NS];
+        page_lds(0, pg);
+        row_load(0, pg, kw[0], vw[0]);
+        page_lds(1, pg);
+        row_load(1, pg, kw[1], vw[1]);
+        page_lds(2, pg);
+        row_load(2, pg, kw[2], vw[2]);
+        page_lds(3, pgn);
+      }
+      if (my_steps > 0) gather_k(kw[0]);
+      stage_store(0, sb[0]);
+      for (int st = 0; st < nst; st += 4) {
+        st_step(st, 0, 0);
+        st_step(st + 1, 1, 1);
+        st_step(st + 2, 2, 0);
+        st_step(st + 3, 3, 1);
+      }
+    }
+  }
+
+  // ---- merge the 8 position slots of each (pair, quarter) and write the
+  //      chunk's partials
+  __syncthreads();                       // every wave is done with the slices
+  float* red = (float*)lds + (size_t)wave * 64 * SW;
+  {
+    float* r = red + lane * SW;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      r[4 * u] = acc[u].x; r[4 * u + 1] = acc[u].y; r[4 * u + 2] = acc[u].z; r[4 * u + 3] = acc[u].w;
+    }
+    r[4 * U] = m;
+    r[4 * U + 1] = l;
+    r[4 * U + 2] = lx;
+  }
+  __syncthreads();
+  // one lane per (pair, quarter): row 2*sv, position slot la == 0
+  if (active && okq[sv] && rp == 0 && la == 0 && p0 < len[sv]) {
+    float M = -INFINITY;
+    for (int i = 0; i < 8; ++i) {
+      const float* r = red + ((2 * sv + (i >> 2)) * 16 + (i & 3) * 4 + lb) * SW;
+      if (r[4 * U + 1] > 0.f) M = fmaxf(M, r[4 * U]);
+    }
+    float4v o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) o[u] = (float4v){0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, LX = 0.f;
+    for (int i = 0; i < 8; ++i) {
+      const float* r = red + ((2 * sv + (i >> 2)) * 16 + (i & 3) * 4 + lb) * SW;
+      if (!(r[4 * U + 1] > 0.f)) continue;
+      const float wt = __builtin_amdgcn_exp2f(r[4 * U] - M);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        o[u].x = fmaf(wt, r[4 * u], o[u].x);
+        o[u].y = fmaf(wt, r[4 * u + 1], o[u].y);
+        o[u].z = fmaf(wt, r[4 * u + 2], o[u].z);
+        o[u].w = fmaf(wt, r[4 * u + 3], o[u].w);
+      }
+      L = fmaf(wt, r[4 * U + 1], L);
+      LX = fmaf(wt, r[4 * U + 2], LX);
+    }
+    const size_t part = (size_t)(h * p.n_pairs + kq[sv]) * p.n_chunks + ch;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float* op = p.part_o + part * D;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int lc = 4 * u;
+      const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
+      *(float4v*)(op + base) = o[u] * inv;
+    }
+    if (lb == 0) p.part_lse[part] = L > 0.f ? M + log2f(LX) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool PG>
+static void launch_split_sp(const DecodeParams& p, int grid, hipStream_t s) {
+  // a step's 16 positions lie in one page when pages hold at least 16
+  // positions; workgroup-shared RoPE rows need eight duos per head
+  if (p.log2P < 4) {
+    hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false, false, PG>), dim3(grid), dim3(512), 0, s, p);
+    return;
+  }
+  if constexpr (!QF32) {
+    if (p.shared_rope) {
+      hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, SHARE, true, true, PG>), dim3(grid), dim3(512), 0, s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true, false, PG>), dim3(grid), dim3(512), 0, s, p);
+}
+
+template <int D, int C, int BITS, bool PG>
+static hipError_t launch_split_t(const DecodeParams& p, bool qf32, int grid, hipStream_t s) {
+  // pairs 2i and 2i+1 belong to one request when the GQA group size is even
+  const bool share = (p.grp & 1) == 0;
+  if (qf32) {
+    if (share) launch_split_sp<D, C, BITS, true, true, PG>(p, grid, s);
+    else launch_split_sp<D, C, BITS, true, false, PG>(p, grid, s);
+  } else {
+    if (share) launch_split_sp<D, C, BITS, false, true, PG>(p, grid, s);
+    else launch_split_sp<D, C, BITS, false, false, PG>(p, grid, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace loopvq

@@ -36,7 +36,7 @@
 
 namespace loopvq {
 
-template <int G, int C, bool XF32, int BITS, bool PAGED>
+template <int G, int C, bool XF32, int BITS, bool PAGED, bool PG>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   constexpr int KD = XF32 ? 2 * G : G;          // reduction length (fp32: high and low halves)
   constexpr int KDP = KD < 16 ? 16 : KD;        // padded to the MFMA depth
@@ -53,11 +53,16 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   __shared__ __attribute__((aligned(16))) float hsl[NTILE * 2 * 16];
 
   const int H = p.H_kv, Tc = p.Tc, D = p.D;
-  const int y = blockIdx.y;
+  // y = ((beta*H + hd)*2 + kv)*NG + gq: with one codebook per channel group
+  // (PG) a workgroup codes group gq only, with that group's codebook
+  const int NG = PG ? D / C : 1;
+  const int gq = PG ? (int)blockIdx.y % NG : 0;
+  const int y = PG ? (int)blockIdx.y / NG : (int)blockIdx.y;
   const int hd = y % H, kv = (y / H) & 1, beta = y / (2 * H);
+  const size_t cbi = ((size_t)(beta * H + hd) * 2 + kv) * NG + gq;   // codebook of this workgroup
 
   // ---- codebook of (beta, hd, kv), permuted to loop-major coordinates
-  const uint16_t* cbsrc = p.cb + ((size_t)(beta * H + hd) * 2 + kv) * KENT * G;
+  const uint16_t* cbsrc = p.cb + cbi * KENT * G;
   for (int x = threadIdx.x; x < KENT * G; x += blockDim.x) {
     const int e = x / G, kap = x - e * G;
     const int m = kap / C, i = kap - m * C;
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   for (int x = threadIdx.x; x < NTILE * 32; x += blockDim.x) {
     const int t = x >> 5, hh = (x >> 4) & 1, q = (x >> 2) & 3, sr = x & 3;
     const int e = 32 * t + 8 * q + 4 * hh + sr;
-    hsl[x] = e < KENT ? -p.hsq[((size_t)(beta * H + hd) * 2 + kv) * KENT + e] : -INFINITY;
+    hsl[x] = e < KENT ? -p.hsq[cbi * KENT + e] : -INFINITY;
   }
   __syncthreads();
 
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   const int R = n * BITS / 8;
   const int P = 1 << p.log2P;
   const void* xsrc = kv ? p.xv : p.xk;
-  const int nvec = p.n_tok * n;        // vectors of this stream
+  const int nvec = PG ? p.n_tok : p.n_tok * n;   // vectors of this stream (PG: of group gq)
   const int nunit = (nvec + 31) >> 5;  // units of 32 vectors
   const int u0 = (blockIdx.x * 4 + wave) * p.units_per_wave;
   const int u1 = min(u0 + p.units_per_wave, nunit);
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   struct Raw { uint32_t w[NMF][NRUN][RW]; };
   auto load_raw = [&](int u, Raw& r) {
     const int v = min(u * 32 + col, nvec - 1);     // clamped: loads stay in bounds
-    const int tok = v >> ln, g = v & (n - 1);
+    const int tok = PG ? v : v >> ln, g = PG ? gq : v & (n - 1);
     size_t tbase;
     if constexpr (PAGED) {
       const int ss = p.src_slot[tok];
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     const int v = u * 32 + col;
     const bool vok = v < nvec;
     const int vc = vok ? v : nvec - 1;
-    const int tok = vc >> ln, g = vc & (n - 1);
+    const int tok = PG ? vc : vc >> ln, g = PG ? gq : vc & (n - 1);
     const int slot = p.slot_mapping[tok];
     // ---- scores against all entries: per 32-entry tile a lane holds 16
     //      entries (rows 8q + 4*hf + s) of its vector.  It keeps the best tile
@@ -278,19 +283,28 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   if (u + 2 < u1) do_unit(u + 2, rb[2], rb[1]);
 }
 
-template <int G, int C, bool XF32, int BITS>
-static hipError_t launch_encode_t(const EncodeParams& p, int n_blocks, hipStream_t s) {
-  dim3 grid(p.n_unit_groups, n_blocks * 2 * p.H_kv);
+template <int G, int C, bool XF32, int BITS, bool PG>
+static hipError_t launch_encode_pg(const EncodeParams& p, int n_blocks, hipStream_t s) {
+  dim3 grid(p.n_unit_groups, n_blocks * 2 * p.H_kv * (PG ? p.D / C : 1));
   if constexpr (!XF32) {
     // bf16 window pages (decode-time page encoding)
     if (p.src_slot != nullptr) {
-      hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true, PG>), grid, dim3(256), 0, s, p);
       return hipGetLastError();
     }
   }
   if (p.src_slot != nullptr) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+template <int G, int C, bool XF32, int BITS>
+static hipError_t launch_encode_t(const EncodeParams& p, int n_blocks, hipStream_t s) {
+  if constexpr (BITS == 8) {
+    if (p.per_group) return launch_encode_pg<G, C, XF32, BITS, true>(p, n_blocks, s);
+  }
+  if (p.per_group) return hipErrorInvalidValue;
+  return launch_encode_pg<G, C, XF32, BITS, false>(p, n_blocks, s);
 }
 
 hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s) {

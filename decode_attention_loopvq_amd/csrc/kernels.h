@@ -67,12 +67,15 @@ struct EncodeParams {
   uint8_t* cache;             // cache of the first block
   int64_t block_stride;
   int n_tok, H_kv, D, c, Tc, K, log2P;
+  int per_group;              // one codebook per channel group: units are 32 tokens of one group
   int units_per_wave;         // units of 32 consecutive (token, group) vectors per wave
   int n_unit_groups;          // ceil(units / (4 * units_per_wave)), the grid's x extent
 };
 
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                hipStream_t s);
+hipError_t launch_decode_split_pg(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
+                                  hipStream_t s);
 hipError_t launch_decode_combine(int D, bool out_bf16, const CombineParams& p, hipStream_t s);
 hipError_t launch_decode_window(int D, bool qf32, const WindowParams& p, int B, hipStream_t s);
 hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s);

@@ -29,9 +29,14 @@
  * Data layouts
  *   codebook  cb     [n_blocks][H_kv][2][K][G] fp16, entry coordinate
  *                    u = i*Tc + m (channel-major, loop-minor), index 1 = K|V.
+ *                    With per_group: [n_blocks][H_kv][2][D/c][K][G], one
+ *                    codebook per channel group (the pages' B_{beta,l,h,g},
+ *                    section "Loop-axis vector quantization").
  *   slices           [T][H_kv][2][K][c] fp16: slice of loop step t (0-based
- *                    here) holds coordinates i*Tc + (t mod Tc) of each entry.
- *   hsq              [n_blocks][H_kv][2][K] fp32: 0.5*||e||^2 of each entry.
+ *                    here) holds coordinates i*Tc + (t mod Tc) of each entry
+ *                    (per_group: [T][H_kv][2][D/c][K][c]).
+ *   hsq              [n_blocks][H_kv][2][K] fp32: 0.5*||e||^2 of each entry
+ *                    (per_group: [n_blocks][H_kv][2][D/c][K]).
  *   index cache      one cache per block beta: [num_pages][H_kv][2][P][R]
  *                    bytes, R = (D/c)*bits/8 bytes per row.  Page p holds the
  *                    rows of tokens p*P .. p*P+P-1 of whichever request maps
@@ -81,6 +86,9 @@ typedef struct loopvq_dims {
   int32_t page_size;  /* tokens per page P: a power of two in [16, 256]                 */
   int32_t x_dtype;    /* encoder input K/V: LOOPVQ_DTYPE_F32 or LOOPVQ_DTYPE_BF16        */
   int32_t io_dtype;   /* decode query and output: LOOPVQ_DTYPE_F32 or LOOPVQ_DTYPE_BF16  */
+  int32_t per_group;  /* 0: one codebook per (block, KV head, K|V), shared by the D/c
+                         channel groups; 1: one codebook per channel group as well
+                         (8-bit codes only)                                             */
 } loopvq_dims;
 /* Supported shapes: D in {64, 128}; D/c a multiple of 8; G = c*Tc in {8, 16, 32}
  * (G = 8 only with fp32 encoder input); 4-bit codes only with K = 16 and

@@ -220,6 +220,35 @@ def make_codebooks(cfg: Config, seed: Optional[int] = None) -> np.ndarray:
     return cb
 
 
+def make_codebooks_per_group(cfg: Config, seed: Optional[int] = None) -> np.ndarray:
+    """fp16 codebooks, one per channel group: [n_blocks, H_kv, 2, D // c, K, G].
+
+    The entries of group g's codebook are K distinct coupled vectors of group g
+    drawn without replacement from the calibration tokens (same generator and
+    channel scales as make_codebooks, seed + 1000 + 500).
+    """
+    seed = (cfg.index if seed is None else seed) + 1500
+    rng = np.random.default_rng(seed)
+    xk, xv = make_kv(cfg, cfg.n_calib, seed=seed)
+    ng = cfg.n_groups
+    cb = np.empty((cfg.n_blocks, cfg.H_kv, 2, ng, cfg.K, cfg.G), dtype=np.float16)
+    ii = np.arange(cfg.c)
+    mm = np.arange(cfg.Tc)
+    for beta in range(cfg.n_blocks):
+        steps = beta * cfg.Tc + mm[None, None, :]
+        for h in range(cfg.H_kv):
+            for kv, x in enumerate((xk, xv)):
+                for g in range(ng):
+                    while True:
+                        tok = rng.choice(cfg.n_calib, size=cfg.K, replace=False)
+                        chans = g * cfg.c + ii[None, :, None]
+                        e = round_to_f16(x[steps, tok[:, None, None], h, chans].reshape(cfg.K, cfg.G))
+                        if len(np.unique(e.view(np.uint16).reshape(cfg.K, -1), axis=0)) == cfg.K:
+                            break
+                    cb[beta, h, kv, g] = e
+    return cb
+
+
 def make_queries(cfg: Config, batch: int, seed: Optional[int] = None, t: int = 0) -> np.ndarray:
     """Decode queries [batch, H_q, D] ~ N(0, 1), already rotated at their own position."""
     seed = (cfg.index if seed is None else seed) + 2000 + t

@@ -68,6 +68,15 @@ def test_invalid_dims(L, kw, status):
     assert L.lib().loopvq_row_bytes(ctypes.byref(_dims(L, **kw))) == status
 
 
+def test_per_group_dims(L):
+    lib = L.lib()
+    assert lib.loopvq_row_bytes(ctypes.byref(_dims(L, per_group=1))) == 32
+    assert lib.loopvq_row_bytes(ctypes.byref(_dims(L, per_group=2))) == -1
+    assert lib.loopvq_row_bytes(ctypes.byref(_dims(L, per_group=1, bits=4))) == -2   # 8-bit codes only
+    assert L.loopvq_dims.make(D=128, c=4, Tc=4, T=4, bits=8, H_kv=1, H_q=1, page_size=64,
+                              per_group=1).n_codebooks == 32
+
+
 def test_bad_K_and_null_dims(L):
     d = _dims(L)
     d.K = 128

@@ -82,3 +82,13 @@ def test_window_split_and_pages():
         for u, p in enumerate(pos):
             assert pages[pt[b, u // 8], 1, 0, u % 8, 3] == b * 10000 + p
             assert pages[pt[b, u // 8], 0, 1, u % 8, 0] == -(b * 10000 + p)
+
+
+def test_per_group_codebooks_hold_their_groups_vectors():
+    cfg = synth.config_by_name("tiny").replace(bits=8, n_calib=300)
+    cb = synth.make_codebooks_per_group(cfg)
+    assert cb.shape == (cfg.n_blocks, cfg.H_kv, 2, cfg.n_groups, cfg.K, cfg.G) and cb.dtype == np.float16
+    for g in (0, cfg.n_groups - 1):
+        e = cb[0, 0, 0, g].view(np.uint16)
+        assert len(np.unique(e, axis=0)) == cfg.K
+    assert not np.array_equal(cb[0, 0, 0, 0], cb[0, 0, 0, 1])
