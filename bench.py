@@ -38,7 +38,7 @@ DECODE_KERNEL = "decode_split_kernel"
 
 def _source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h", "kernels.h"):
+    for f in ("decode_split.h", "decode.hip", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
