@@ -9,4 +9,5 @@ from .workloads import (  # noqa: F401
     loop_correlated, channel_scales, make_kv, make_codebooks, make_queries,
     make_seq_lens, make_block_table, slot_mapping_for, random_index_cache, make_kv_torch,
     make_window, window_positions, fill_window_pages, make_codebooks_per_group,
+    make_tasq, make_sigma, codebooks_from_vectors,
 )

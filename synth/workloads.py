@@ -386,3 +386,56 @@ def fill_window_pages(num_pages: int, page_table: np.ndarray, n_sink: np.ndarray
         pages[pg, :, 0, u % 8, :] = k_of(b, pos)
         pages[pg, :, 1, u % 8, :] = v_of(b, pos)
     return pages
+
+
+# --------------------------------------------------------------------------
+# TaSQ inputs (synthetic stand-ins for calibrated ones)
+# --------------------------------------------------------------------------
+def make_tasq(cfg: Config, seed: Optional[int] = None):
+    """Synthetic TaSQ parameters of one layer.
+
+    w    [T, H_kv, D] float32 channel weights, lognormal(0, 0.4): TaSQ sets
+         w_i^2 proportional to the second moment of the queries on channel i,
+         which needs a model; any positive weights exercise the same path.
+    perm [T // Tc, H_kv, D/2] int32: one uniformly random pair permutation per
+         (block, head), standing in for the covariance-based grouping.
+    Seed: config index + 5000.
+    """
+    seed = (cfg.index if seed is None else seed) + 5000
+    rng = np.random.default_rng(seed)
+    w = np.exp(0.4 * rng.standard_normal((cfg.T, cfg.H_kv, cfg.D))).astype(np.float32)
+    perm = np.stack([np.stack([rng.permutation(cfg.D // 2) for _ in range(cfg.H_kv)])
+                     for _ in range(cfg.n_blocks)]).astype(np.int32)
+    return w, perm
+
+
+def make_sigma(n: int, seed: int) -> np.ndarray:
+    """Positive fp16 per-token scales (lognormal(0, 0.3)), float16 [n]."""
+    rng = np.random.default_rng(seed)
+    return np.exp(0.3 * rng.standard_normal(n)).astype(np.float16)
+
+
+def codebooks_from_vectors(cfg: Config, xk: np.ndarray, xv: np.ndarray, seed: int) -> np.ndarray:
+    """fp16 codebooks [n_blocks, H_kv, 2, K, G] of K distinct coupled vectors
+    sampled without replacement from the given per-step arrays xk, xv
+    [T, n, H_kv, D] (the same sampling rule as make_codebooks, on any data,
+    for example keys already mapped to another coordinate system)."""
+    rng = np.random.default_rng(seed)
+    n = xk.shape[1]
+    cb = np.empty((cfg.n_blocks, cfg.H_kv, 2, cfg.K, cfg.G), dtype=np.float16)
+    n_vec = n * cfg.n_groups
+    ii = np.arange(cfg.c)
+    mm = np.arange(cfg.Tc)
+    for beta in range(cfg.n_blocks):
+        for h in range(cfg.H_kv):
+            for kv, x in enumerate((xk, xv)):
+                while True:
+                    pick = rng.choice(n_vec, size=cfg.K, replace=False)
+                    tok, grp = pick // cfg.n_groups, pick % cfg.n_groups
+                    steps = beta * cfg.Tc + mm[None, None, :]
+                    chans = grp[:, None, None] * cfg.c + ii[None, :, None]
+                    e = round_to_f16(np.asarray(x)[steps, tok[:, None, None], h, chans].reshape(cfg.K, cfg.G))
+                    if len(np.unique(e.view(np.uint16).reshape(cfg.K, -1), axis=0)) == cfg.K:
+                        break
+                cb[beta, h, kv] = e
+    return cb
