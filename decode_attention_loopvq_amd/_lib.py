@@ -60,6 +60,11 @@ class loopvq_bf16_window(ctypes.Structure):
                 ("n_sink", ctypes.c_void_p), ("win_start", ctypes.c_void_p)]
 
 
+class loopvq_tasq(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("sigma", ctypes.c_void_p),
+                ("sigma_stride", ctypes.c_int64)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -102,6 +107,15 @@ def lib() -> ctypes.CDLL:
         L.loopvq_decode_attn_window.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I,
                                                 ctypes.POINTER(loopvq_bf16_window), ctypes.c_float,
                                                 P, P, P, ctypes.c_size_t, P]
+        L.loopvq_encode_tasq_workspace_bytes.restype = ctypes.c_size_t
+        L.loopvq_encode_tasq_workspace_bytes.argtypes = [D, I, I]
+        L.loopvq_encode_tasq.restype = ctypes.c_int
+        L.loopvq_encode_tasq.argtypes = [D, I, I, I, P, P, ctypes.POINTER(loopvq_tasq), P, P, P, P,
+                                         ctypes.c_int64, P, ctypes.c_size_t, P]
+        L.loopvq_decode_attn_tasq.restype = ctypes.c_int
+        L.loopvq_decode_attn_tasq.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.POINTER(loopvq_tasq),
+                                              ctypes.POINTER(loopvq_bf16_window), ctypes.c_float,
+                                              P, P, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -110,7 +124,8 @@ EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_s
             "loopvq_rope_table", "loopvq_rope_table_floats", "loopvq_encode", "loopvq_encode_pages",
             "loopvq_decode_workspace_bytes",
             "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine",
-            "loopvq_decode_attn_window")
+            "loopvq_decode_attn_window", "loopvq_encode_tasq_workspace_bytes", "loopvq_encode_tasq",
+            "loopvq_decode_attn_tasq")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -310,4 +325,88 @@ def loopvq_decode_attn_window(dims: loopvq_dims, t: int, q: torch.Tensor, index_
                                            int(max_pages), _ptr(seq_lens), int(max_seq_len), ctypes.byref(win),
                                            float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                            int(workspace.numel()), _stream()), "loopvq_decode_attn_window")
+    return out, lse
+
+
+def _tasq_struct(dims: loopvq_dims, w: torch.Tensor, perm: torch.Tensor, sigma: torch.Tensor) -> loopvq_tasq:
+    """w [T][H_kv][D] fp32, perm [T/Tc][H_kv][D/2] int32, sigma [T][n_slots] fp16 (device tensors)."""
+    _need(w, torch.float32, "tasq w"); _need(perm, torch.int32, "tasq perm"); _need(sigma, torch.float16, "sigma")
+    if tuple(w.shape) != (dims.T, dims.H_kv, dims.D) or tuple(perm.shape) != (dims.n_blocks, dims.H_kv, dims.D // 2):
+        raise ValueError("tasq: w must be [T][H_kv][D] and perm [T/Tc][H_kv][D/2]")
+    if sigma.dim() != 2 or sigma.shape[0] != dims.T:
+        raise ValueError("sigma must be [T][n_slots]")
+    return loopvq_tasq(w.data_ptr(), perm.data_ptr(), sigma.data_ptr(), int(sigma.shape[1]))
+
+
+def loopvq_encode_tasq_workspace_bytes(dims: loopvq_dims, n_tok: int, n_blocks: int) -> int:
+    return int(lib().loopvq_encode_tasq_workspace_bytes(ctypes.byref(dims), int(n_tok), int(n_blocks)))
+
+
+def loopvq_encode_tasq(dims: loopvq_dims, xk: torch.Tensor, xv: torch.Tensor, w: torch.Tensor,
+                       perm: torch.Tensor, sigma: torch.Tensor, cb: torch.Tensor, hsq: torch.Tensor,
+                       slot_mapping: torch.Tensor, index_cache: torch.Tensor, first_block: int = 0,
+                       n_blocks: Optional[int] = None, block_stride_bytes: Optional[int] = None,
+                       workspace: Optional[torch.Tensor] = None) -> None:
+    """loopvq_encode with TaSQ-coded keys; writes each token's fp16 sigma of every coded loop step
+    into sigma [T][n_slots] at its slot.  cb holds codebooks of u for the keys."""
+    xdt = torch.float32 if dims.x_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+    _need(xk, xdt, "xk"); _need(xv, xdt, "xv")
+    _need(cb, torch.float16, "cb"); _need(hsq, torch.float32, "hsq")
+    _need(slot_mapping, torch.int32, "slot_mapping"); _need(index_cache, torch.uint8, "index_cache")
+    tq = _tasq_struct(dims, w, perm, sigma)
+    if n_blocks is None:
+        n_blocks = xk.shape[0] // dims.Tc
+    n_tok = xk.shape[1]
+    if xk.shape != xv.shape or xk.shape[0] != n_blocks * dims.Tc or slot_mapping.numel() != n_tok:
+        raise ValueError("encode_tasq: inconsistent shapes")
+    if block_stride_bytes is None:
+        block_stride_bytes = index_cache.numel() // max(n_blocks, 1) if n_blocks > 1 else 0
+    need = loopvq_encode_tasq_workspace_bytes(dims, n_tok, n_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xk.device)
+    _check(lib().loopvq_encode_tasq(ctypes.byref(dims), n_tok, first_block, n_blocks, _ptr(xk), _ptr(xv),
+                                    ctypes.byref(tq), _ptr(cb), _ptr(hsq), _ptr(slot_mapping), _ptr(index_cache),
+                                    int(block_stride_bytes), _ptr(workspace), int(workspace.numel()), _stream()),
+           "loopvq_encode_tasq")
+
+
+def loopvq_decode_attn_tasq(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: torch.Tensor,
+                            slices: torch.Tensor, rope_table: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, w: torch.Tensor, perm: torch.Tensor,
+                            sigma: torch.Tensor, window: Optional[tuple] = None, sm_scale: float = 0.0,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, max_pos: Optional[int] = None):
+    """Decode attention at loop step t over TaSQ-coded keys; window = (kv_bf16, page_table, n_sink,
+    win_start) adds the bf16 sink and recent window.  Returns (out, lse)."""
+    iodt = torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+    _need(q, iodt, "q"); _need(index_cache, torch.uint8, "index_cache")
+    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
+    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
+    tq = _tasq_struct(dims, w, perm, sigma)
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.H_q, dims.D), dtype=iodt, device=q.device)
+    _need(out, iodt, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if max_pos is None:
+        raise ValueError("max_pos (positions covered by rope_table) is required")
+    win = None
+    if window is not None:
+        kv_bf16, page_table, n_sink, win_start = window
+        _need(kv_bf16, torch.bfloat16, "kv_bf16"); _need(page_table, torch.int32, "page_table")
+        _need(n_sink, torch.int32, "n_sink"); _need(win_start, torch.int32, "win_start")
+        win = loopvq_bf16_window(kv_bf16.data_ptr(), page_table.data_ptr(),
+                                 page_table.shape[1] if page_table.dim() == 2 else 0,
+                                 n_sink.data_ptr(), win_start.data_ptr())
+    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+    _check(lib().loopvq_decode_attn_tasq(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
+                                         _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
+                                         int(max_pages), _ptr(seq_lens), int(max_seq_len), ctypes.byref(tq),
+                                         None if win is None else ctypes.byref(win), float(sm_scale),
+                                         _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()),
+                                         _stream()), "loopvq_decode_attn_tasq")
     return out, lse

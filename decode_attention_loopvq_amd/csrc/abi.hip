@@ -93,6 +93,17 @@ bool decode_supported(int D, int c, int bits) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOOPVQ_OK : LOOPVQ_ERR_HIP; }
 
+// TaSQ-coded keys: 8-bit codes with one codebook per (block, head, K|V), the
+// shapes the TaSQ decode kernels are compiled for
+int check_tasq(const loopvq_dims* d, const loopvq_tasq* tq) {
+  int st = check_dims(d);
+  if (st != LOOPVQ_OK) return st;
+  if (tq == nullptr || !tq->w || !tq->perm || !tq->sigma || tq->sigma_stride < 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (d->T > 1 && tq->sigma_stride == 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (d->bits != 8 || d->per_group) return LOOPVQ_ERR_UNSUPPORTED;
+  return LOOPVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,11 +166,12 @@ size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D) {
 
 }  // extern "C"
 
-// shared by the dense and the paged-bf16 encode entry points
+// shared by the dense, paged-bf16 and TaSQ encode entry points: codes
+// streams kv_lo .. kv_lo + kv_n - 1 of {K, V}, inputs fp32 when xf32
 static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
                        const void* xk, const void* xv, const int32_t* src_slot, int64_t step_stride,
                        const void* cb, const float* hsq, const int32_t* slot_mapping, uint8_t* index_cache,
-                       int64_t block_stride_bytes, hipStream_t stream) {
+                       int64_t block_stride_bytes, int kv_lo, int kv_n, bool xf32, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != LOOPVQ_OK) return st;
   const int nb_total = dims->T / dims->Tc;
@@ -188,16 +200,20 @@ static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   p.K = dims->K;
   p.log2P = ilog2(dims->page_size);
   p.per_group = dims->per_group;
+  p.kv_lo = kv_lo;
+  p.kv_n = kv_n;
   // units of 32 (token, group) vectors (per group: 32 tokens of one group);
   // about 8192 waves over the whole call
-  const long long streams = (long long)n_blocks * 2 * H * n_codebook_groups(dims);
+  const long long streams = (long long)n_blocks * kv_n * H * n_codebook_groups(dims);
   const long long units = dims->per_group ? ((long long)n_tok + 31) / 32
                                           : ((long long)n_tok * (dims->D / dims->c) + 31) / 32;
   long long upw = (streams * units + 8191) / 8192;
   upw = std::max<long long>(1, std::min<long long>(upw, units));
   p.units_per_wave = (int)upw;
   p.n_unit_groups = (int)((units + 4 * upw - 1) / (4 * upw));
-  return hip_status(launch_encode(G, dims->x_dtype == LOOPVQ_DTYPE_F32, dims->bits, p, n_blocks, stream));
+  // fp32 input needs the fp32 instantiation (G = 8 exists only there)
+  if (!xf32 && G == 8) return LOOPVQ_ERR_UNSUPPORTED;
+  return hip_status(launch_encode(G, xf32, dims->bits, p, n_blocks, stream));
 }
 
 extern "C" {
@@ -209,7 +225,7 @@ int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, i
   if (check_dims(dims) != LOOPVQ_OK) return check_dims(dims);
   const int64_t step_stride = (int64_t)std::max(n_tok, 0) * dims->H_kv * dims->D;
   return encode_impl(dims, n_tok, first_block, n_blocks, xk, xv, nullptr, step_stride, cb, hsq, slot_mapping,
-                     index_cache, block_stride_bytes, stream);
+                     index_cache, block_stride_bytes, 0, 2, dims->x_dtype == LOOPVQ_DTYPE_F32, stream);
 }
 
 int loopvq_encode_pages(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
@@ -226,7 +242,53 @@ int loopvq_encode_pages(const loopvq_dims* dims, int32_t n_tok, int32_t first_bl
   // block beta of this call reads loop steps (beta - first_block)*Tc .. of the pools
   const void* xv = kv_pages ? (const void*)((const uint16_t*)kv_pages + 8 * dims->D) : nullptr;
   return encode_impl(dims, n_tok, first_block, n_blocks, kv_pages, xv, src_slot, step_stride, cb, hsq,
-                     slot_mapping, index_cache, block_stride_bytes, stream);
+                     slot_mapping, index_cache, block_stride_bytes, 0, 2, false, stream);
+}
+
+size_t loopvq_encode_tasq_workspace_bytes(const loopvq_dims* dims, int32_t n_tok, int32_t n_blocks) {
+  if (check_dims(dims) != LOOPVQ_OK || n_tok < 0 || n_blocks < 0) return 0;
+  return align256((size_t)n_blocks * dims->Tc * n_tok * dims->H_kv * dims->D * sizeof(float));
+}
+
+int loopvq_encode_tasq(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
+                       const void* xk, const void* xv, const loopvq_tasq* tasq, const void* cb,
+                       const float* hsq, const int32_t* slot_mapping, uint8_t* index_cache,
+                       int64_t block_stride_bytes, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  int st = check_tasq(dims, tasq);
+  if (st != LOOPVQ_OK) return st;
+  const int nb_total = dims->T / dims->Tc;
+  if (n_tok < 0 || first_block < 0 || n_blocks < 1 || first_block + n_blocks > nb_total)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (n_tok == 0) return LOOPVQ_OK;
+  if (!xk || !xv || !slot_mapping || !workspace) return LOOPVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (workspace_bytes < loopvq_encode_tasq_workspace_bytes(dims, n_tok, n_blocks)) return LOOPVQ_ERR_WORKSPACE;
+  // the rest of the checks are the encoder's, made before anything is launched
+  if (!cb || !hsq || !index_cache || (n_blocks > 1 && block_stride_bytes <= 0)) return LOOPVQ_ERR_INVALID_ARG;
+  if ((dims->D / dims->c) % 16 != 0) return LOOPVQ_ERR_UNSUPPORTED;
+  TasqParams tp{};
+  tp.xk = xk;
+  tp.w = tasq->w;
+  tp.perm = tasq->perm;
+  tp.slot_mapping = slot_mapping;
+  tp.sigma = tasq->sigma;
+  tp.sigma_stride = tasq->sigma_stride;
+  tp.u = (float*)workspace;
+  tp.n_tok = n_tok;
+  tp.H = dims->H_kv;
+  tp.D = dims->D;
+  tp.Tc = dims->Tc;
+  tp.first_step = first_block * dims->Tc;
+  st = hip_status(launch_tasq_transform(dims->x_dtype == LOOPVQ_DTYPE_F32, tp, n_blocks * dims->Tc, stream));
+  if (st != LOOPVQ_OK) return st;
+  const int64_t step_stride = (int64_t)n_tok * dims->H_kv * dims->D;
+  // keys: the codes of u (fp32); values: as loopvq_encode
+  st = encode_impl(dims, n_tok, first_block, n_blocks, workspace, workspace, nullptr, step_stride, cb, hsq,
+                   slot_mapping, index_cache, block_stride_bytes, 0, 1, true, stream);
+  if (st != LOOPVQ_OK) return st;
+  return encode_impl(dims, n_tok, first_block, n_blocks, xv, xv, nullptr, step_stride, cb, hsq, slot_mapping,
+                     index_cache, block_stride_bytes, 1, 1, dims->x_dtype == LOOPVQ_DTYPE_F32, stream);
 }
 
 size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {
@@ -251,7 +313,7 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
                       const uint8_t* index_cache, const void* slices, const float* rope_table,
                       int32_t max_pos, const int32_t* block_table, int32_t max_pages,
                       const int32_t* seq_lens, const int32_t* seq_lo, int32_t max_seq_len, float sm_scale,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, const loopvq_tasq* tasq, hipStream_t stream) {
   int st = check_decode_common(dims, B, max_seq_len);
   if (st != LOOPVQ_OK) return st;
   if (t < 1 || t > dims->T || max_pos < 0 || max_pages < 0) return LOOPVQ_ERR_INVALID_ARG;
@@ -291,6 +353,13 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)dims->D);
   p.scale_log2 = scale * 1.4426950408889634f;
   const bool qf32 = dims->io_dtype == LOOPVQ_DTYPE_F32;
+  if (tasq != nullptr) {
+    // step t's weights, its block's permutations and its sigma array
+    p.tq_w = tasq->w + (size_t)(t - 1) * dims->H_kv * dims->D;
+    p.tq_perm = tasq->perm + (size_t)((t - 1) / dims->Tc) * dims->H_kv * (dims->D / 2);
+    p.tq_sigma = tasq->sigma + (size_t)(t - 1) * tasq->sigma_stride;
+    return hip_status(launch_decode_split_tq(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
+  }
   if (dims->per_group) return hip_status(launch_decode_split_pg(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
   return hip_status(launch_decode_split(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
 }
@@ -334,7 +403,7 @@ int loopvq_decode_split(const loopvq_dims* dims, int32_t t, int32_t B, const voi
                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
   return split_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages, seq_lens,
-                    nullptr, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+                    nullptr, max_seq_len, sm_scale, workspace, workspace_bytes, nullptr, stream);
 }
 
 int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq_lens, int32_t max_seq_len,
@@ -357,12 +426,16 @@ int loopvq_decode_attn(const loopvq_dims* dims, int32_t t, int32_t B, const void
   return loopvq_decode_combine(dims, B, seq_lens, max_seq_len, out, lse, workspace, workspace_bytes, stream);
 }
 
-int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
-                              const uint8_t* index_cache, const void* slices, const float* rope_table,
-                              int32_t max_pos, const int32_t* block_table, int32_t max_pages,
-                              const int32_t* seq_lens, int32_t max_seq_len, const loopvq_bf16_window* window,
-                              float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream) {
+}  // extern "C"
+
+// coded positions through the split pass, bf16 sink and window through the
+// window kernel, then the combine; tasq: TaSQ-coded keys, or null
+static int window_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                       const uint8_t* index_cache, const void* slices, const float* rope_table,
+                       int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                       const int32_t* seq_lens, int32_t max_seq_len, const loopvq_bf16_window* window,
+                       float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       const loopvq_tasq* tasq, hipStream_t stream) {
   int st = check_decode_common(dims, B, max_seq_len);
   if (st != LOOPVQ_OK) return st;
   if (window == nullptr) return LOOPVQ_ERR_INVALID_ARG;
@@ -378,7 +451,8 @@ int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B, con
   if (workspace_bytes < pl.total()) return LOOPVQ_ERR_WORKSPACE;
   // coded positions [n_sink, win_start)
   st = split_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages,
-                  window->win_start, window->n_sink, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+                  window->win_start, window->n_sink, max_seq_len, sm_scale, workspace, workspace_bytes, tasq,
+                  stream);
   if (st != LOOPVQ_OK) return st;
   WindowParams wp{};
   wp.q = q;
@@ -401,6 +475,38 @@ int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B, con
   st = hip_status(launch_decode_window(dims->D, dims->io_dtype == LOOPVQ_DTYPE_F32, wp, B, stream));
   if (st != LOOPVQ_OK) return st;
   return combine_impl(dims, B, window->win_start, max_seq_len, out, lse, workspace, workspace_bytes, true, stream);
+}
+
+extern "C" {
+
+int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                              const uint8_t* index_cache, const void* slices, const float* rope_table,
+                              int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t max_seq_len, const loopvq_bf16_window* window,
+                              float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return window_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages, seq_lens,
+                     max_seq_len, window, sm_scale, out, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+int loopvq_decode_attn_tasq(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                            const uint8_t* index_cache, const void* slices, const float* rope_table,
+                            int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, int32_t max_seq_len, const loopvq_tasq* tasq,
+                            const loopvq_bf16_window* window, float sm_scale, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_decode_common(dims, B, max_seq_len);
+  if (st != LOOPVQ_OK) return st;
+  st = check_tasq(dims, tasq);
+  if (st != LOOPVQ_OK) return st;
+  if (window != nullptr)
+    return window_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages, seq_lens,
+                       max_seq_len, window, sm_scale, out, lse, workspace, workspace_bytes, tasq, stream);
+  if (B > 0 && out == nullptr) return LOOPVQ_ERR_INVALID_ARG;
+  st = split_impl(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages, seq_lens,
+                  nullptr, max_seq_len, sm_scale, workspace, workspace_bytes, tasq, stream);
+  if (st != LOOPVQ_OK) return st;
+  return combine_impl(dims, B, seq_lens, max_seq_len, out, lse, workspace, workspace_bytes, false, stream);
 }
 
 }  // extern "C"

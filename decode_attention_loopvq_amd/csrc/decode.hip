@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p) {
 // ---------------------------------------------------------------- dispatch
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                hipStream_t s) {
-#define LVQ_CASE(d, c, b) if (D == d && C == c && bits == b) return launch_split_t<d, c, b, false>(p, qf32, grid, s);
+#define LVQ_CASE(d, c, b) if (D == d && C == c && bits == b) return launch_split_t<d, c, b, false, false>(p, qf32, grid, s);
   LVQ_CASE(128, 4, 8) LVQ_CASE(128, 8, 8) LVQ_CASE(128, 2, 8)
   LVQ_CASE(128, 4, 4) LVQ_CASE(128, 8, 4) LVQ_CASE(128, 2, 4)
   LVQ_CASE(64, 2, 4) LVQ_CASE(64, 4, 4) LVQ_CASE(64, 2, 8) LVQ_CASE(64, 4, 8) LVQ_CASE(64, 8, 8)

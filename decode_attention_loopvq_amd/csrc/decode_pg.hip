@@ -7,7 +7,7 @@ namespace loopvq {
 
 hipError_t launch_decode_split_pg(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                   hipStream_t s) {
-#define LVQ_CASE(d, c, b) if (D == d && C == c && bits == b) return launch_split_t<d, c, b, true>(p, qf32, grid, s);
+#define LVQ_CASE(d, c, b) if (D == d && C == c && bits == b) return launch_split_t<d, c, b, true, false>(p, qf32, grid, s);
   LVQ_CASE(128, 4, 8) LVQ_CASE(128, 8, 8) LVQ_CASE(128, 2, 8)
   LVQ_CASE(64, 2, 8) LVQ_CASE(64, 4, 8) LVQ_CASE(64, 8, 8)
 #undef LVQ_CASE

@@ -35,6 +35,22 @@
 //  * RoPE rows come from a table interleaved by groups of 4 positions (one
 //    contiguous 256-byte run per 16 lanes); with eight duos per head the
 //    workgroup stages each step's rows once into an LDS ring (see below).
+//  * TaSQ-coded keys (TQ) [appendix "Orthogonal application with TaSQ",
+//    "Formulation" and "Grouping under loop coupling"]: the codes index
+//    u = P(w k / sigma), whose codes hold whole RoPE pairs (u channels 2p,
+//    2p+1 = key channels perm[p], perm[p] + D/2).  The lane's frequencies
+//    become the u pairs of its quarter's groups: one 32-bit word of an entry is
+//    the (f, f + D/2) pair of a key column, so no byte perms are needed.  The
+//    channel weights fold into the query operand, which is then no longer an
+//    fp16 value: the MFMA's reduction index carries it as an fp16 high and low
+//    part against the same pair twice, A row = (x_f hi, x_h hi, x_f lo, x_h lo)
+//    and B column = (u_f, u_h, u_f, u_h), so products stay exact and one MFMA
+//    covers both pairs of a duo when they share keys.  P reorders the RoPE
+//    frequencies: the shared rows are written into the LDS ring in the head's
+//    frequency order (two 8-byte stores per staged piece, at offsets fixed for
+//    the kernel's life), and per-wave rows are read by 8-byte loads at fixed
+//    per-lane offsets.  sigma multiplies each score in the V role; it is
+//    loaded with the step's V index rows.
 #pragma once
 
 #include <math.h>
@@ -97,7 +113,7 @@ __device__ __forceinline__ Entry<EB> lds_entry(const uint8_t* lds, uint32_t addr
   return e;
 }
 
-template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP, bool ST, bool PG>
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP, bool ST, bool PG, bool TQ>
 __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   constexpr int N = D / C;            // groups per row
   constexpr int Q = N / 8;            // lo (and hi) groups per lane quarter
@@ -126,6 +142,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
                                                                           : LDS_MERGE;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int wsteps[WAVES];
+  __shared__ int tqinv[TQ ? D / 2 : 1];     // TaSQ: u pair of each RoPE frequency
 
   // ---- workgroup -> (KV head, 8 work items).  Heads vary fastest, so each
   //      XCD (blocks of one residue mod 8, renumbered contiguously) owns a
@@ -160,6 +177,13 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         uint32_t t = *(const uint32_t*)sp; v = (uint4v){t, t, t, t};
       }
       *(uint4v*)(lds + ke * 256 + cchunk * 16) = v;
+    }
+  }
+  if constexpr (TQ) {
+    // inverse of the head's pair permutation (out-of-range entries are ignored)
+    if (threadIdx.x < D / 2) {
+      const int f = p.tq_perm[h * (D / 2) + threadIdx.x];
+      if ((unsigned)f < (unsigned)(D / 2)) tqinv[f] = threadIdx.x;
     }
   }
   __syncthreads();
@@ -209,8 +233,37 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      key column (k0_f, k0_h, k1_f, k1_h) of a position the MFMA yields
   //      X0, Y0, X1, Y1 of that position.
   half4v AK[F];
-  half4v AKl[QF32 ? F : 1];
-  if (active) {
+  half4v AKl[(QF32 && !TQ) ? F : 1];
+  // TaSQ: u pair of the lane's i-th frequency slot: the pairs of its quarter's
+  // lo groups, then those of its hi groups
+  auto tq_upair = [&](int i) { return i < F / 2 ? la * (F / 2) + i : D / 4 + la * (F / 2) + (i - F / 2); };
+  auto tq_freq = [&](int i) { return min(max(p.tq_perm[h * (D / 2) + tq_upair(i)], 0), D / 2 - 1); };
+  if (active && TQ) {
+    // row lb of the block-diagonal query matrix over (u_f, u_h) with the
+    // weights folded in, [[q0_f/w_f, q0_h/w_h], [q0_h/w_f, -q0_f/w_h]] (+) pair 1,
+    // each coefficient as fp16 high and low parts along the reduction index
+    const int s = lb >> 1;
+    const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
+    const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
+    const size_t qrow = ((size_t)bb * p.H_q + jq) * D;
+    const float* wrow = p.tq_w + (size_t)h * D;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      const int f = tq_freq(i);
+      float a, c;
+      if constexpr (QF32) {
+        a = ((const float*)p.q)[qrow + f];
+        c = ((const float*)p.q)[qrow + f + D / 2];
+      } else {
+        a = u2f((uint32_t)((const uint16_t*)p.q)[qrow + f] << 16);
+        c = u2f((uint32_t)((const uint16_t*)p.q)[qrow + f + D / 2] << 16);
+      }
+      const float x0 = ((lb & 1) ? c : a) / wrow[f];
+      const float x1 = ((lb & 1) ? -a : c) / wrow[f + D / 2];
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      AK[i] = (half4v){h0, h1, (_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
+    }
+  } else if (active) {
     const int s = lb >> 1;
     const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
     const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
@@ -229,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
       const _Float16 z = (_Float16)0.f;
       AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
-      if constexpr (QF32) {
+      if constexpr (QF32 && !TQ) {
         const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
         AKl[i] = s ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
       }
@@ -289,18 +342,24 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   };
   // K rows of both streams at the lane's K position, V rows of stream sv at
   // the lane's two V positions
-  auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW]) {
+  // (TaSQ: also the fp16 sigma of the lane's two V positions, issued before
+  // the V rows so that waiting for the rows covers them)
+  auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW], uint32_t* sg) {
     const uint8_t* vbase;
+    size_t vslot;                               // first slot of the V rows' group (page*P + offset)
     if constexpr (SP) {
       const uint8_t* base[2];
+      size_t slot0[2];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int page = has[s] ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
         const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
         base[s] = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+        slot0[s] = (size_t)page * P + (gs & (P - 1)) + 8 * rp;
         RowLoad<LB>::load(base[s] + kro, kw[s]);
       }
       vbase = (NS == 1 || sv == 0) ? base[0] : base[NS - 1];
+      vslot = (NS == 1 || sv == 0) ? slot0[0] : slot0[NS - 1];
     } else {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -311,6 +370,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const int page = has[sv] ? raw_page[NS] : 0;
       const int gs = min(p0 + st * NT + 8 * rp, last[sv]) & ~7;
       vbase = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
+      vslot = (size_t)page * P + (gs & (P - 1));
+    }
+    if constexpr (TQ) {
+      const uint16_t* sp = p.tq_sigma + vslot + la;
+      sg[0] = sp[0];
+      sg[1] = sp[4];
     }
     RowLoad<LB>::load(vbase + vro, vw[0]);
     RowLoad<LB>::load(vbase + vro + 4 * R, vw[1]);
@@ -320,11 +385,33 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // lanes of a row (4 positions x 4 quarters) read one contiguous 256-B run,
   // and the rows of one step form one contiguous TSTEP-byte block
   float4v tb[FP];
+  // TaSQ, per-wave rows: byte offsets of the lane's frequency slots 2j, 2j+1
+  // inside its row of the interleaved table (low / high 16 bits)
+  uint32_t toff[(TQ && !ST) ? FP : 1];
+  if constexpr (TQ && !ST) {
+    auto off = [&](int i) {
+      const int f = tq_freq(i);
+      return (uint32_t)(((f % F) >> 1) * 256 + (f / F) * 64 + (f & 1) * 8);
+    };
+#pragma unroll
+    for (int j = 0; j < FP; ++j) toff[j] = off(2 * j) | (off(2 * j + 1) << 16);
+  }
+  const uint32_t tbo_row = (uint32_t)((row * FP * 16 + lb) * 16);
   auto table_load = [&](int st) {
     const int gt = min(p0 + st * NT, glast);
-    const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
+    if constexpr (TQ && !ST) {
+      const uint8_t* tr = (const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo_row;
 #pragma unroll
-    for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
+      for (int j = 0; j < FP; ++j) {
+        const float2v a = *(const float2v*)(tr + (toff[j] & 0xffffu));
+        const float2v b = *(const float2v*)(tr + (toff[j] >> 16));
+        tb[j] = (float4v){a.x, a.y, b.x, b.y};
+      }
+    } else {
+      const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
+#pragma unroll
+      for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
+    }
   };
 
   auto entry_addr = [&](const uint32_t* w, int s, uint32_t off) {
@@ -354,15 +441,35 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      lane's quarter; klo/khi and tb hold the step's entries and rows)
   auto k_side = [&](float* sc) {
     float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      const int r = i / C, e = i % C;                      // entry and element of frequency i
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
-      const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
-      const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
-      float4v xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
+      float4v xy;
+      if constexpr (TQ) {
+        // u pair i of the quarter: word e of entry r of the lo (first F/2) or
+        // hi groups holds (u_f, u_h)
+        constexpr int PE = C / 2;
+        const bool hq = i >= F / 2;
+        const int r = (hq ? i - F / 2 : i) / PE, e = (hq ? i - F / 2 : i) % PE;
+        const uint32_t w0 = hq ? khi[0][r].d[e] : klo[0][r].d[e];
+        xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w0, w0}), zero, 0, 0, 0);
+        if constexpr (!SHARE) {
+          // pair 1 reads its own keys: rows 2-3 of a second product
+          const uint32_t w1 = hq ? khi[NS - 1][r].d[e] : klo[NS - 1][r].d[e];
+          const float4v xy1 =
+              __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w1, w1}), zero, 0, 0, 0);
+          xy.z = xy1.z;
+          xy.w = xy1.w;
+        }
+      } else {
+        const int r = i / C, e = i % C;                      // entry and element of frequency i
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
+        const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
+        const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
+        xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, zero, 0, 0, 0);
+        if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
+      }
       const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
       const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
       sa0 = fmaf(cs, xy.x, sa0);
@@ -372,10 +479,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     // interleave: each MFMA is followed by VALU work (the next perms and this
     // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
+    constexpr int KMF = TQ ? (SHARE ? 1 : 2) : (QF32 ? 2 : 1);
+    constexpr int KVALU = TQ ? 4 : 6;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QF32 ? 2 : 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, KMF, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, KVALU, 0);
     }
     sc[0] = sa0 + sb0;
     sc[1] = sa1 + sb1;
@@ -397,11 +506,17 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      lazy max) and the V side: acc += p * v on the matrix cores (block =
   //      one token); p is rounded to fp16 for the product, and l adds the same
   //      rounded p, so the output stays an exact convex combination
-  auto v_side = [&](int g0, const float* sv2) {
+  auto v_side = [&](int g0, const float* sv2, const uint32_t* sg) {
     const int posa = g0 + vrel;
     const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 4) < vspan;
-    const float sa = va ? sv2[0] * p.scale_log2 : -INFINITY;
-    const float sb = vb ? sv2[1] * p.scale_log2 : -INFINITY;
+    float s0 = sv2[0], s1 = sv2[1];
+    if constexpr (TQ) {
+      // the rebuilt key is sigma * P^-1(u_hat) / w: the score scales by sigma
+      s0 *= (float)__builtin_bit_cast(_Float16, (uint16_t)sg[0]);
+      s1 *= (float)__builtin_bit_cast(_Float16, (uint16_t)sg[1]);
+    }
+    const float sa = va ? s0 * p.scale_log2 : -INFINITY;
+    const float sb = vb ? s1 * p.scale_log2 : -INFINITY;
     const float smax = fmaxf(sa, sb);
     const bool need = smax > m + LAZY_TAU;
     if (__ballot(need) != 0) {
@@ -468,38 +583,44 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       // step reloads tb for st+1 and gathers step st+1 as soon as the
       // registers free up, then refills (kwn, vwn) with the rows of st+3
       // (page ids pgr, read two steps earlier) and reads the pages of st+5.
-      auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], int* pgr) {
+      // (TaSQ: sigma of a step travels with its index rows, and moves to sgc
+      // when the step's V entries are gathered, before the rows are refilled)
+      uint32_t sgc[2] = {0u, 0u};
+      auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], uint32_t* sgn, int* pgr) {
         float sc[2], sv2[2];
         k_side(sc);
         table_load(st + 1);                             // RoPE rows of step st+1
         to_v_role(sc, sv2);
         gather_k(kwn);                                  // K entries of step st+1
-        v_side(p0 + st * NT, sv2);
+        v_side(p0 + st * NT, sv2, sgc);
         gather_v(vwn);                                  // V entries of step st+1
-        row_load(st + 3, pgr, kwn, vwn);
+        if constexpr (TQ) { sgc[0] = sgn[0]; sgc[1] = sgn[1]; }
+        row_load(st + 3, pgr, kwn, vwn, sgn);
         page_at(st + 5, pgr);
       };
       uint32_t kwA[NS][LW], vwA[2][LW], kwB[NS][LW], vwB[2][LW];
+      uint32_t sgA[2], sgB[2];
       int pgA[NPG], pgB[NPG], pg0[NPG];
       page_at(0, pg0);
-      row_load(0, pg0, kwA, vwA);
+      row_load(0, pg0, kwA, vwA, sgA);
       page_at(1, pg0);
-      row_load(1, pg0, kwB, vwB);
+      row_load(1, pg0, kwB, vwB, sgB);
       table_load(0);
       gather_k(kwA);
       gather_v(vwA);
+      if constexpr (TQ) { sgc[0] = sgA[0]; sgc[1] = sgA[1]; }
       page_at(2, pg0);
-      row_load(2, pg0, kwA, vwA);
+      row_load(2, pg0, kwA, vwA, sgA);
       page_at(3, pgB);
       page_at(4, pgA);
       // an active wave has steps >= 2; the first two steps are peeled so that
       // the loads outstanding at the loop head are in the same order on entry
       // and on the back edge (the wait counts at the head are then tight)
-      do_step(0, kwB, vwB, pgB);
-      do_step(1, kwA, vwA, pgA);
+      do_step(0, kwB, vwB, sgB, pgB);
+      do_step(1, kwA, vwA, sgA, pgA);
       for (int st = 2; st < steps; st += 2) {
-        do_step(st, kwB, vwB, pgB);
-        do_step(st + 1, kwA, vwA, pgA);
+        do_step(st, kwB, vwB, sgB, pgB);
+        do_step(st + 1, kwA, vwA, sgA, pgA);
       }
     }
   } else {
@@ -533,8 +654,32 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const int gt = min(p0 + st * NT, glast_st);
       if (lane < PIECES) dst = ((const float4v*)p.rope)[(size_t)(gt >> 2) * FP * 16 + wave * PIECES + lane];
     };
+    // TaSQ: the piece's two frequencies go to the slots of their u pairs, so
+    // that the ring holds the rows in this head's frequency order
+    uint32_t sd0 = 0, sd1 = 0;
+    if constexpr (TQ) {
+      const int pc = wave * PIECES + lane;
+      const int n_ = pc & 3, la_ = (pc >> 2) & 3, j_ = (pc >> 4) % FP, row_ = (pc >> 4) / FP;
+      auto dest = [&](int f) {
+        const int pp = min(max(tqinv[f], 0), D / 2 - 1);   // in range even for a bad permutation
+        const bool hq = pp >= D / 4;
+        const int pr = hq ? pp - D / 4 : pp;
+        const int la2 = pr / (F / 2), i2 = (hq ? F / 2 : 0) + pr % (F / 2);
+        return (uint32_t)((((row_ * FP + (i2 >> 1)) * 4 + la2) * 4 + n_) * 16 + (i2 & 1) * 8);
+      };
+      sd0 = dest(la_ * F + 2 * j_);
+      sd1 = dest(la_ * F + 2 * j_ + 1);
+    }
     auto stage_store = [&](int st, const float4v& v) {
-      if (lane < PIECES) *(float4v*)(lds + LDS_SLICES + (st & 1) * TSTEP + (wave * PIECES + lane) * 16) = v;
+      if (lane < PIECES) {
+        uint8_t* ring = lds + LDS_SLICES + (st & 1) * TSTEP;
+        if constexpr (TQ) {
+          *(float2v*)(ring + sd0) = (float2v){v.x, v.y};
+          *(float2v*)(ring + sd1) = (float2v){v.z, v.w};
+        } else {
+          *(float4v*)(ring + (wave * PIECES + lane) * 16) = v;
+        }
+      }
     };
     auto table_lds = [&](int st) {
       const uint8_t* ring = lds + LDS_SLICES + (st & 1) * TSTEP + tbo;
@@ -554,7 +699,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       for (int s = 0; s < NS; ++s)
         pg[s] = plist[s * PGMAX + min((min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
     };
-    uint32_t kw[4][NS][LW], vw[4][2][LW];
+    uint32_t kw[4][NS][LW], vw[4][2][LW], sg[4][2];
     int pgn[NS];                             // page ids of step st+3, read during step st-1
     // one step: index rows of step x live in row buffer x % 4, staged pieces
     // alternate with b2 = st % 2.  Every global load of a step (staged rows,
@@ -567,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     auto st_step = [&](int st, int b4, int b2) {
       wg_barrier();                                   // ring slot st&1 holds the rows of st
       stage_load(st + 2, sb[b2]);
-      row_load(st + 3, pgn, kw[(b4 + 3) & 3], vw[(b4 + 3) & 3]);
+      row_load(st + 3, pgn, kw[(b4 + 3) & 3], vw[(b4 + 3) & 3], sg[(b4 + 3) & 3]);
       page_lds(st + 4, pgn);
       __builtin_amdgcn_sched_barrier(0);
       if (st < my_steps) {
@@ -580,7 +725,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         to_v_role(sc, sv2);
         gather_k(kw[(b4 + 1) & 3]);                   // K entries of step st+1
         __builtin_amdgcn_sched_barrier(0);
-        v_side(p0 + st * NT, sv2);
+        v_side(p0 + st * NT, sv2, sg[b4]);
         __builtin_amdgcn_sched_barrier(0);
       }
       stage_store(st + 1, sb[1 - b2]);
@@ -591,11 +736,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       {
         int pg[NS];
         page_lds(0, pg);
-        row_load(0, pg, kw[0], vw[0]);
+        row_load(0, pg, kw[0], vw[0], sg[0]);
         page_lds(1, pg);
-        row_load(1, pg, kw[1], vw[1]);
+        row_load(1, pg, kw[1], vw[1], sg[1]);
         page_lds(2, pg);
-        row_load(2, pg, kw[2], vw[2]);
+        row_load(2, pg, kw[2], vw[2], sg[2]);
         page_lds(3, pgn);
       }
       if (my_steps > 0) gather_k(kw[0]);
@@ -663,33 +808,36 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, int C, int BITS, bool QF32, bool SHARE, bool PG>
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool PG, bool TQ>
 static void launch_split_sp(const DecodeParams& p, int grid, hipStream_t s) {
   // a step's 16 positions lie in one page when pages hold at least 16
   // positions; workgroup-shared RoPE rows need eight duos per head
   if (p.log2P < 4) {
-    hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false, false, PG>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false, false, PG, TQ>), dim3(grid), dim3(512), 0,
+                       s, p);
     return;
   }
   if constexpr (!QF32) {
     if (p.shared_rope) {
-      hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, SHARE, true, true, PG>), dim3(grid), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, SHARE, true, true, PG, TQ>), dim3(grid), dim3(512), 0,
+                         s, p);
       return;
     }
   }
-  hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true, false, PG>), dim3(grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true, false, PG, TQ>), dim3(grid), dim3(512), 0, s,
+                     p);
 }
 
-template <int D, int C, int BITS, bool PG>
+template <int D, int C, int BITS, bool PG, bool TQ>
 static hipError_t launch_split_t(const DecodeParams& p, bool qf32, int grid, hipStream_t s) {
   // pairs 2i and 2i+1 belong to one request when the GQA group size is even
   const bool share = (p.grp & 1) == 0;
   if (qf32) {
-    if (share) launch_split_sp<D, C, BITS, true, true, PG>(p, grid, s);
-    else launch_split_sp<D, C, BITS, true, false, PG>(p, grid, s);
+    if (share) launch_split_sp<D, C, BITS, true, true, PG, TQ>(p, grid, s);
+    else launch_split_sp<D, C, BITS, true, false, PG, TQ>(p, grid, s);
   } else {
-    if (share) launch_split_sp<D, C, BITS, false, true, PG>(p, grid, s);
-    else launch_split_sp<D, C, BITS, false, false, PG>(p, grid, s);
+    if (share) launch_split_sp<D, C, BITS, false, true, PG, TQ>(p, grid, s);
+    else launch_split_sp<D, C, BITS, false, false, PG, TQ>(p, grid, s);
   }
   return hipGetLastError();
 }

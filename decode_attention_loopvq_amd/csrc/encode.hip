@@ -53,12 +53,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   __shared__ __attribute__((aligned(16))) float hsl[NTILE * 2 * 16];
 
   const int H = p.H_kv, Tc = p.Tc, D = p.D;
-  // y = ((beta*H + hd)*2 + kv)*NG + gq: with one codebook per channel group
+  // y = ((beta*kv_n + kv - kv_lo)*H + hd)*NG + gq: with one codebook per channel group
   // (PG) a workgroup codes group gq only, with that group's codebook
   const int NG = PG ? D / C : 1;
   const int gq = PG ? (int)blockIdx.y % NG : 0;
   const int y = PG ? (int)blockIdx.y / NG : (int)blockIdx.y;
-  const int hd = y % H, kv = (y / H) & 1, beta = y / (2 * H);
+  const int hd = y % H, kv = p.kv_lo + (y / H) % p.kv_n, beta = y / (p.kv_n * H);
   const size_t cbi = ((size_t)(beta * H + hd) * 2 + kv) * NG + gq;   // codebook of this workgroup
 
   // ---- codebook of (beta, hd, kv), permuted to loop-major coordinates
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
 
 template <int G, int C, bool XF32, int BITS, bool PG>
 static hipError_t launch_encode_pg(const EncodeParams& p, int n_blocks, hipStream_t s) {
-  dim3 grid(p.n_unit_groups, n_blocks * 2 * p.H_kv * (PG ? p.D / C : 1));
+  dim3 grid(p.n_unit_groups, n_blocks * p.kv_n * p.H_kv * (PG ? p.D / C : 1));
   if constexpr (!XF32) {
     // bf16 window pages (decode-time page encoding)
     if (p.src_slot != nullptr) {

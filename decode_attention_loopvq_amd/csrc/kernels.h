@@ -15,6 +15,11 @@ struct DecodeParams {
   const int32_t* block_table; // [B][max_pages]
   const int32_t* seq_lens;    // [B] end of each request's coded positions
   const int32_t* seq_lo;      // [B] first coded position (bf16 sink before it), or null for 0
+  // TaSQ-coded keys (null unless the TaSQ variant runs): the codes index
+  // u = P(w k / sigma); the key is rebuilt as sigma * P^-1(u_hat) / w
+  const float* tq_w;          // [H_kv][D] channel weights of this loop step
+  const int32_t* tq_perm;     // [H_kv][D/2] pair permutation of this block
+  const uint16_t* tq_sigma;   // fp16 scale of this loop step per physical slot (page*P + offset)
   float* part_o;              // [H_kv][n_pairs][n_chunks][D]
   float* part_lse;            // [H_kv][n_pairs][n_chunks], log2 domain
   int B, H_kv, H_q, grp, max_pages, log2P;
@@ -68,17 +73,33 @@ struct EncodeParams {
   int64_t block_stride;
   int n_tok, H_kv, D, c, Tc, K, log2P;
   int per_group;              // one codebook per channel group: units are 32 tokens of one group
+  int kv_lo, kv_n;            // code streams kv_lo .. kv_lo + kv_n - 1 of {K, V}
   int units_per_wave;         // units of 32 consecutive (token, group) vectors per wave
   int n_unit_groups;          // ceil(units / (4 * units_per_wave)), the grid's x extent
+};
+
+// TaSQ key transform: u = P(w k / sigma) and the fp16 sigma of every token
+struct TasqParams {
+  const void* xk;             // [n_steps][n_tok][H][D] pre-RoPE keys, bf16 or fp32
+  const float* w;             // [T][H][D] channel weights
+  const int32_t* perm;        // [T/Tc][H][D/2] pair permutations
+  const int32_t* slot_mapping;  // [n_tok] physical slot of each token
+  uint16_t* sigma;            // fp16 scale of loop step t, slot s at t*sigma_stride + s
+  int64_t sigma_stride;
+  float* u;                   // [n_steps][n_tok][H][D] fp32
+  int n_tok, H, D, Tc, first_step;
 };
 
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                hipStream_t s);
 hipError_t launch_decode_split_pg(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                   hipStream_t s);
+hipError_t launch_decode_split_tq(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
+                                  hipStream_t s);
 hipError_t launch_decode_combine(int D, bool out_bf16, const CombineParams& p, hipStream_t s);
 hipError_t launch_decode_window(int D, bool qf32, const WindowParams& p, int B, hipStream_t s);
 hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s);
+hipError_t launch_tasq_transform(bool xf32, const TasqParams& p, int n_steps, hipStream_t s);
 hipError_t launch_build_slices(const uint16_t* cb, uint16_t* slices, float* hsq, int n_blocks, int H_kv,
                                int K, int c, int Tc, hipStream_t s);
 

@@ -301,6 +301,76 @@ int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B,
                               void* out, float* lse, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * TaSQ-coded keys (TaSQ+LoopVQ).  [LoopVQ paper, appendix "Orthogonal
+ * application with TaSQ": "Formulation" (eqs. (10)-(11)), "Grouping under
+ * loop coupling", "Calibration and bitwidth".]  Before coupling, the pre-RoPE
+ * key of loop step t, head h and token j is mapped to
+ *     u = P_{beta,h}(w_{t,h} (.) k / sigma_{t,j}),
+ * sigma_{t,j} being the root mean square of w_{t,h} (.) k over all heads and
+ * channels of token j at step t, kept in fp16 (round to nearest even; a
+ * token whose fp16 sigma is 0 gets u = 0).  P moves RoPE pairs as units and
+ * keeps each pair inside one code: u channel 2p holds key channel perm[p] and
+ * u channel 2p+1 holds perm[p] + D/2.  Keys are coded from u (values as
+ * usual), and decode rebuilds k_hat = sigma * P^-1(u_hat) / w before RoPE.
+ *   w             [T][H_kv][D] fp32 channel weights, positive; |q_i / w_i|
+ *                 must stay inside fp16's range.
+ *   perm          [T/Tc][H_kv][D/2] int32, each row a permutation of
+ *                 0 .. D/2-1 (other values give unspecified results).
+ *   sigma         fp16 scales: loop step t (0-based), physical slot s
+ *                 (page*P + offset) at sigma[t*sigma_stride + s].  Written by
+ *                 loopvq_encode_tasq, read by loopvq_decode_attn_tasq.
+ *   sigma_stride  elements between the arrays of consecutive loop steps
+ *                 (> 0 when T > 1).
+ * TaSQ-coded keys need 8-bit codes and one codebook per (block, head, K|V)
+ * (per_group = 0); other shapes return LOOPVQ_ERR_UNSUPPORTED.  The K
+ * codebooks are codebooks of u.
+ */
+typedef struct loopvq_tasq {
+  const float* w;
+  const int32_t* perm;
+  uint16_t* sigma;
+  int64_t sigma_stride;
+} loopvq_tasq;
+
+/* Workspace bytes of loopvq_encode_tasq (u of every coded loop step, fp32). */
+size_t loopvq_encode_tasq_workspace_bytes(const loopvq_dims* dims, int32_t n_tok,
+                                          int32_t n_blocks);
+
+/*
+ * loopvq_encode with TaSQ-coded keys: computes sigma (stored at each token's
+ * slot for every coded loop step) and u, then codes u as the keys and xv as
+ * the values.  Arguments as for loopvq_encode; xk holds the pre-RoPE keys.
+ * workspace: at least loopvq_encode_tasq_workspace_bytes(dims, n_tok,
+ * n_blocks) bytes, 256-byte aligned.  The key codes differ from an exact
+ * evaluation only where two distances lie within fp32 rounding of each other
+ * (u is formed in fp64 and rounded once to fp32), and sigma only where the
+ * exact RMS lies within fp64 rounding of an fp16 rounding midpoint.
+ */
+int loopvq_encode_tasq(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
+                       int32_t n_blocks, const void* xk, const void* xv,
+                       const loopvq_tasq* tasq, const void* cb, const float* hsq,
+                       const int32_t* slot_mapping, uint8_t* index_cache,
+                       int64_t block_stride_bytes, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decode attention at loop step t over TaSQ-coded keys: reads w of step t,
+ * perm of block (t-1)/Tc and the sigma array of step t.  With window non-NULL
+ * the bf16 sink and recent window are attended as in loopvq_decode_attn_window
+ * (their keys are plain pre-RoPE keys); with window NULL this is
+ * loopvq_decode_attn.  Other arguments as for those calls.
+ */
+int loopvq_decode_attn_tasq(const loopvq_dims* dims, int32_t t, int32_t B,
+                            const void* q, const uint8_t* index_cache,
+                            const void* slices, const float* rope_table,
+                            int32_t max_pos, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens,
+                            int32_t max_seq_len, const loopvq_tasq* tasq,
+                            const loopvq_bf16_window* window, float sm_scale,
+                            void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

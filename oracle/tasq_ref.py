@@ -46,7 +46,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .loopvq_ref import (attention, gather_rows, rebuild, rope, slots_to_groups,
+from .loopvq_ref import (attention, gather_rows, gather_rows_at, rebuild, rope, slots_to_groups,
                          unpack_rows, coupled_vectors)
 
 # relative half-width of the band around an fp16 rounding midpoint inside
@@ -169,6 +169,50 @@ def decode_attention_tasq(q: np.ndarray, cache_block: np.ndarray, block_table_ro
         krot = rope(khat, pos, base)
         for j in range(h * grp, (h + 1) * grp):
             o[j], lse[j] = attention(q[j], krot, vhat, sm_scale)
+    return o, lse
+
+
+def decode_attention_tasq_window(q: np.ndarray, cache_block: np.ndarray, block_table_row: np.ndarray,
+                                 n: int, n_sink: int, win_start: int, k_bf: np.ndarray, v_bf: np.ndarray,
+                                 cb_block: np.ndarray, t: int, Tc: int, c: int, bits: int, base: float,
+                                 w_t: np.ndarray, perm_b: np.ndarray, sigma_pos: np.ndarray,
+                                 sm_scale: float | None = None):
+    """Decode attention over a cache mixing bf16 tokens and TaSQ-coded keys.
+
+    As loopvq_ref.decode_attention_window [P1 section "System implementation":
+    bf16 sink and recent window, codes elsewhere, one softmax over all tokens],
+    except that the coded positions [n_sink, win_start) rebuild their keys as in
+    decode_attention_tasq.  The bf16 tokens hold plain pre-RoPE keys (the
+    transform applies only when a token is coded).  sigma_pos [n] is read only
+    at coded positions.  Returns (o [H_q, D], lse [H_q]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H_q, D = q.shape
+    H_kv = cache_block.shape[1]
+    grp = H_q // H_kv
+    assert 0 <= n_sink <= win_start <= n
+    m = (t - 1) % Tc
+    sm_scale = 1.0 / np.sqrt(D) if sm_scale is None else sm_scale
+    ng = D // c
+    qpos = np.arange(n_sink, win_start)
+    bpos = np.concatenate([np.arange(n_sink), np.arange(win_start, n)]).astype(np.int64)
+    k_bf = np.asarray(k_bf, dtype=np.float64)
+    v_bf = np.asarray(v_bf, dtype=np.float64)
+    sig = np.asarray(sigma_pos, dtype=np.float64)
+    o = np.zeros((H_q, D))
+    lse = np.zeros(H_q)
+    for h in range(H_kv):
+        k = np.empty((n, D))
+        v = np.empty((n, D))
+        ki = slots_to_groups(unpack_rows(gather_rows_at(cache_block, block_table_row, qpos, h, 0), bits, ng))
+        vi = slots_to_groups(unpack_rows(gather_rows_at(cache_block, block_table_row, qpos, h, 1), bits, ng))
+        k[qpos] = tasq_inverse(rebuild(ki, cb_block[h, 0], Tc, c, m), w_t[h], perm_b[h], sig[qpos])
+        v[qpos] = rebuild(vi, cb_block[h, 1], Tc, c, m)
+        k[bpos] = k_bf[bpos, h]
+        v[bpos] = v_bf[bpos, h]
+        krot = rope(k, np.arange(n), base)
+        for j in range(h * grp, (h + 1) * grp):
+            o[j], lse[j] = attention(q[j], krot, v, sm_scale)
     return o, lse
 
 

@@ -86,6 +86,30 @@ class GpuLayer:
                 None if lse is None else lse.cpu().numpy().astype(np.float64))
 
 
+    def decode_tasq(self, t, q, cache_block, block_table, seq_lens, w, perm, sigma, window=None,
+                    max_seq_len=None, want_lse=True):
+        """TaSQ-coded keys: w [T][H_kv][D], perm [T/Tc][H_kv][D/2], sigma [T][n_slots] fp16 (numpy or
+        device tensors); window = (kv_pages, page_table, n_sink, win_start) or None."""
+        q_d = q if isinstance(q, torch.Tensor) else io_tensor(self.cfg, q)
+        cache_d = cache_block if isinstance(cache_block, torch.Tensor) else to_dev(cache_block)
+        i32 = lambda a: a if isinstance(a, torch.Tensor) else to_dev(np.asarray(a, dtype=np.int32))
+        w_d = w if isinstance(w, torch.Tensor) else to_dev(np.asarray(w, np.float32))
+        sig_d = sigma if isinstance(sigma, torch.Tensor) else to_dev(np.asarray(sigma, np.float16))
+        msl = int(np.max(seq_lens)) if max_seq_len is None else max_seq_len
+        lse = torch.empty((q_d.shape[0], self.cfg.H_q), dtype=torch.float32, device="cuda") if want_lse else None
+        win = None
+        if window is not None:
+            kvp, pt, ns, ws = window
+            kv_d = kvp if isinstance(kvp, torch.Tensor) else to_dev(np.asarray(kvp, np.float32), torch.bfloat16)
+            win = (kv_d, i32(pt), i32(ns), i32(ws))
+        out, lse = lv.loopvq_decode_attn_tasq(self.dims, t, q_d, cache_d, self.slices, self.rope, i32(block_table),
+                                              i32(seq_lens), msl, w_d, i32(perm), sig_d, window=win, lse=lse,
+                                              max_pos=self.max_pos)
+        torch.cuda.synchronize()
+        return (out.float().cpu().numpy().astype(np.float64),
+                None if lse is None else lse.cpu().numpy().astype(np.float64))
+
+
 def ref_decode_window(cfg, t, q, cache_block, block_table, seq_lens, cb, n_sink, win_start, kv_of,
                       requests=None, heads=None):
     """Oracle output with bf16 sink/window tokens; kv_of(b, h) -> (k [n, D], v [n, D]) bf16 values of
@@ -181,3 +205,40 @@ def check_codes(cfg, got_cache, xk, xv, cb, slots, heads=None, blocks=None, meth
                 ok = oracle.accepts(z, E, res, got)
                 bad += int((~ok).sum())
     return ties, bad
+
+
+def sigma_at_positions(sigma_t, block_table_row, n, page_size):
+    """sigma of loop step t at positions 0..n-1 of one request (slot-indexed array -> by position)."""
+    pos = np.arange(n)
+    slots = np.asarray(block_table_row, np.int64)[pos // page_size] * page_size + pos % page_size
+    return np.asarray(sigma_t, np.float64)[slots]
+
+
+def ref_decode_tasq(cfg, t, q, cache_block, block_table, seq_lens, cb, w, perm, sigma, requests=None,
+                    heads=None, window=None):
+    """Oracle output with TaSQ-coded keys.  sigma [T][n_slots] (fp16 values); window = (n_sink,
+    win_start, kv_of) adds the bf16 sink and recent window (kv_of(b, h) -> (k [n, D], v [n, D]))."""
+    tq = oracle.tasq_ref
+    grp = cfg.H_q // cfg.H_kv
+    beta = (t - 1) // cfg.Tc
+    requests = range(len(seq_lens)) if requests is None else requests
+    heads = range(cfg.H_kv) if heads is None else heads
+    res = {}
+    for b in requests:
+        n = int(seq_lens[b])
+        sig = sigma_at_positions(sigma[t - 1], block_table[b], n, cfg.page_size)
+        for h in heads:
+            rows = slice(h * grp, (h + 1) * grp)
+            qb = np.asarray(q[b], np.float64)[rows]
+            args = (cb[beta, h:h + 1], t, cfg.Tc, cfg.c, cfg.bits, cfg.base, w[t - 1, h:h + 1],
+                    perm[beta, h:h + 1], sig)
+            if window is None:
+                o, lse = tq.decode_attention_tasq(qb, cache_block[:, h:h + 1], block_table[b], n, *args)
+            else:
+                ns, ws, kv_of = window
+                k, v = kv_of(b, h)
+                o, lse = tq.decode_attention_tasq_window(qb, cache_block[:, h:h + 1], block_table[b], n,
+                                                         int(ns[b]), int(ws[b]), k[:, None, :], v[:, None, :],
+                                                         *args)
+            res[(b, h)] = (o, lse)
+    return res

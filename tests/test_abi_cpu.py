@@ -169,6 +169,44 @@ def test_encode_pages_validation_before_launch(L):
     assert call(n_tok=0, pages=None, src=None) == 0
 
 
+def test_tasq_validation_before_launch(L):
+    lib = L.lib()
+    d = _dims(L)
+    F = 1 << 20
+    good = L.loopvq_tasq(F, F, F, 4096)
+    ws_enc = L.loopvq_encode_tasq_workspace_bytes(d, 10, 1)
+    assert ws_enc == ((4 * 10 * 16 * 128 * 4 + 255) // 256) * 256
+    def enc(n_tok=10, first=0, nb=1, tq=good, ptr=FAKE, ws=ws_enc, work=FAKE, dims=d):
+        t = None if tq is None else ctypes.byref(tq)
+        return lib.loopvq_encode_tasq(ctypes.byref(dims), n_tok, first, nb, ptr, ptr, t, ptr, ptr, ptr, ptr, 0,
+                                      work, ws, None)
+    assert enc(tq=None) == -1
+    for bad in (L.loopvq_tasq(None, F, F, 4096), L.loopvq_tasq(F, None, F, 4096), L.loopvq_tasq(F, F, None, 4096),
+                L.loopvq_tasq(F, F, F, 0), L.loopvq_tasq(F, F, F, -1)):
+        assert enc(tq=bad) == -1
+    assert enc(ws=ws_enc - 1) == -3
+    assert enc(work=ctypes.c_void_p(F + 16)) == -1            # workspace not 256-byte aligned
+    assert enc(ptr=None) == -1
+    assert enc(n_tok=-1) == -1
+    assert enc(nb=2) == -1
+    assert enc(dims=_dims(L, bits=4)) == -2                   # TaSQ keys: 8-bit codes only
+    assert enc(dims=_dims(L, per_group=1)) == -2
+    assert enc(n_tok=0, ptr=None) == 0
+    ws = L.loopvq_decode_workspace_bytes(d, 4, 1000)
+    def dec(t=1, B=4, tq=good, ptr=FAKE, ws_bytes=ws, dims=d, win=None):
+        q = None if tq is None else ctypes.byref(tq)
+        w = None if win is None else ctypes.byref(win)
+        return lib.loopvq_decode_attn_tasq(ctypes.byref(dims), t, B, ptr, ptr, ptr, ptr, 1000, ptr, 16, ptr, 1000,
+                                           q, w, 0.0, ptr, None, FAKE, ws_bytes, None)
+    assert dec(tq=None) == -1
+    assert dec(t=0) == -1
+    assert dec(ptr=None) == -1
+    assert dec(ws_bytes=ws - 1) == -3
+    assert dec(dims=_dims(L, bits=4)) == -2
+    assert dec(win=L.loopvq_bf16_window(None, F, 4, F, F)) == -1
+    assert dec(B=0) == 0
+
+
 def test_slices_validation(L):
     lib = L.lib()
     assert lib.loopvq_build_codebook_slices(ctypes.byref(_dims(L)), None, FAKE, None, None) == -1

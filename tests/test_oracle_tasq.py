@@ -211,6 +211,48 @@ def test_tasq_decode_permutation_acts_on_pairs():
     np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("split", ["all_coded", "all_bf16", "mixed"])
+def test_tasq_window_reduces_to_its_parts(split):
+    # no bf16 tokens: the TaSQ decode; no coded tokens: the plain bf16-window
+    # decode (the transform never touches bf16 keys); mixed: the coded part
+    # through the TaSQ rebuild and the bf16 part as stored (lossless codebook
+    # case -> textbook attention over the original keys)
+    rng = np.random.default_rng(24)
+    T, Tc, c, D, N, bits, H = 4, 4, 2, 16, 6, 8, 1
+    k, w = _exact_tasq_case(rng, T, N, H, D)
+    v = rng.standard_normal((T, N, H, D)).astype(np.float16).astype(np.float64)
+    perm = np.array([[rng.permutation(D // 2)]])
+    u, s16 = tq.tasq_transform(k, w, perm, Tc)
+    cb = np.zeros((1, H, 2, 256, c * Tc), dtype=np.float16)
+    for kv, x in enumerate((u, v)):
+        z = oracle.coupled_vectors(x[:, :, 0, :], Tc, c, 0).reshape(-1, c * Tc)
+        fill = 100.0 + np.arange(256 - len(z))[:, None] + rng.random((256 - len(z), c * Tc))
+        cb[0, 0, kv] = np.concatenate([z, fill]).astype(np.float16)
+    P = 8
+    bt = np.array([[0]], dtype=np.int32)
+    caches, _, _ = oracle.build_index_cache(u, v, cb, Tc, c, bits, synth.slot_mapping_for(bt, 0, N, P), 1, P)
+    ns, ws = {"all_coded": (0, N), "all_bf16": (N, N), "mixed": (2, 4)}[split]
+    t = 3
+    q = rng.standard_normal((1, D))
+    o, lse = tq.decode_attention_tasq_window(q, caches[0], bt[0], N, ns, ws, k[t - 1], v[t - 1], cb[0], t, Tc, c,
+                                             bits, 1e4, w[t - 1], perm[0], s16[t - 1])
+    if split == "all_coded":
+        o2, l2 = tq.decode_attention_tasq(q, caches[0], bt[0], N, cb[0], t, Tc, c, bits, 1e4, w[t - 1], perm[0],
+                                          s16[t - 1])
+    elif split == "all_bf16":
+        o2, l2 = oracle.decode_attention_window(q, caches[0], bt[0], N, N, N, k[t - 1], v[t - 1], cb[0], t, Tc,
+                                                c, bits, 1e4)
+    else:
+        krot = oracle.rope(k[t - 1, :, 0, :], np.arange(N), 1e4)
+        o2 = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q)[None, None], torch.tensor(krot)[None, None],
+            torch.tensor(v[t - 1, :, 0, :])[None, None])[0, 0].numpy()
+        s = (krot @ q[0]) / math.sqrt(D)
+        l2 = [s.max() + math.log(np.exp(s - s.max()).sum())]
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l2, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- k-means
 def test_kmeans_hand_worked():
     z = np.array([[0.0], [1.0], [10.0], [11.0]])
