@@ -12,8 +12,9 @@ GPU encoder from synthetic loop-correlated keys and values.  Two more legs
 are reported beside the headline: the same batch with a 64-token bf16 sink
 and a 256-token bf16 recent window ("window"), the decode-time coding of
 one 8-token window page per request ("page_encode"), the split pass with one
-codebook per channel group ("per_group"), and the encoder on the
-prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode").
+codebook per channel group ("per_group"), TaSQ-coded keys on the same batch
+and the TaSQ transform + coding of the prefill ("tasq"), and the encoder on
+the prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode").
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -233,6 +234,81 @@ def bench_per_group(args, torch, np, synth, lv, dec):
                         "in LDS"}
 
 
+def bench_tasq(args, torch, np, synth, lv, dec):
+    """TaSQ-coded keys on the same 32K batch: the whole decode call (split pass with
+    the weight-folded query, permuted RoPE rows and per-token sigma, then the
+    combine), and the transform + coding of the 1.4B-layer prefill."""
+    cfg, dims, lens = dec["cfg"], dec["dims"], dec["lens"]
+    B, max_seq_len = len(lens), dec["max_seq_len"]
+    w_np, perm_np = synth.make_tasq(cfg)
+    w, perm = torch.from_numpy(w_np).cuda(), torch.from_numpy(perm_np).cuda()
+    n_slots = dec["cache"].shape[1] * cfg.page_size
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.index + 7000)
+    sigma = torch.exp(0.3 * torch.randn((cfg.T, n_slots), generator=g, device="cuda")).to(torch.float16)
+    out = torch.empty((B, cfg.H_q, cfg.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device="cuda")
+    wsp = torch.empty(lv.loopvq_decode_workspace_bytes(dims, B, max_seq_len), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        t = i % cfg.T + 1
+        lv.loopvq_decode_attn_tasq(dims, t, dec["qs"][t - 1], dec["cache"][0], dec["slices"], dec["rope"],
+                                   dec["bt"], dec["seq"], max_seq_len, w, perm, sigma, out=out, lse=lse,
+                                   workspace=wsp, max_pos=max_seq_len)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    res = {"metric": "decode-attn cached tokens/s with TaSQ-coded keys", "ms_per_call": round(ms, 5),
+           "value": round(float(lens.sum()) / (ms * 1e-3), 1), "unit": "cached tokens/s",
+           "workload": f"{cfg.name} batch, synthetic w and P, per-token fp16 sigma (2 bytes per token "
+                       "and loop step beside the index rows)",
+           "sigma_bytes_per_call": int(lens.sum()) * 2}
+    if args.skip_encode:
+        return res
+    ecfg = synth.config_by_name("layer1p4b")
+    n_tok = ecfg.encode_batch * ecfg.encode_tokens
+    elens = np.full(ecfg.encode_batch, ecfg.encode_tokens)
+    bt_np, num_pages = synth.make_block_table(ecfg, elens)
+    slots = torch.from_numpy(np.concatenate([synth.slot_mapping_for(bt_np, b, int(n), ecfg.page_size)
+                                             for b, n in enumerate(elens)])).cuda()
+    edims = lv.loopvq_dims.make(D=ecfg.D, c=ecfg.c, Tc=ecfg.Tc, T=ecfg.T, bits=ecfg.bits, H_kv=ecfg.H_kv,
+                                H_q=ecfg.H_q, page_size=ecfg.page_size, x_dtype=ecfg.x_dtype,
+                                io_dtype=ecfg.io_dtype)
+    cb = torch.from_numpy(synth.make_codebooks(ecfg)).cuda()
+    _, hsq = lv.loopvq_build_codebook_slices(edims, cb)
+    xk, xv = synth.make_kv_torch(ecfg, n_tok, 78)
+    ew, eperm = (torch.from_numpy(a).cuda() for a in synth.make_tasq(ecfg))
+    esig = torch.zeros((ecfg.T, num_pages * ecfg.page_size), dtype=torch.float16, device="cuda")
+    cache = torch.zeros((num_pages, ecfg.H_kv, 2, ecfg.page_size, ecfg.row_bytes), dtype=torch.uint8,
+                        device="cuda")
+    ews = torch.empty(lv.loopvq_encode_tasq_workspace_bytes(edims, n_tok, ecfg.n_blocks), dtype=torch.uint8,
+                      device="cuda")
+    reps = max(3, args.steps // 4)
+    for _ in range(2):
+        lv.loopvq_encode_tasq(edims, xk, xv, ew, eperm, esig, cb, hsq, slots, cache, workspace=ews)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        lv.loopvq_encode_tasq(edims, xk, xv, ew, eperm, esig, cb, hsq, slots, cache, workspace=ews)
+    e1.record()
+    torch.cuda.synchronize()
+    ems = e0.elapsed_time(e1) / reps
+    vecs = n_tok * ecfg.H_kv * 2 * ecfg.n_groups * ecfg.n_blocks
+    res["encode"] = {"metric": "encode vecs/s with TaSQ-coded keys", "value": round(vecs / (ems * 1e-3), 1),
+                     "unit": "coupled vectors/s", "ms_per_call": round(ems, 5),
+                     "workload": f"{ecfg.name}: transform + coding of {ecfg.encode_batch} x {ecfg.encode_tokens} "
+                                 "tokens (keys from fp32 u, values from bf16)"}
+    del ews, xk, xv
+    return res
+
+
 def bench_page_encode(args, torch, np, synth, lv, dec):
     """Decode-time page encoding at the 32K batch's shape: the oldest 8-token bf16
     window page of each of the 16 requests, coded for all loop steps at once."""
@@ -364,6 +440,7 @@ def main():
     win = bench_window(args, torch, np, synth, lv, dec)
     penc = bench_page_encode(args, torch, np, synth, lv, dec)
     pgr = bench_per_group(args, torch, np, synth, lv, dec)
+    tqr = bench_tasq(args, torch, np, synth, lv, dec)
     enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
     cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
     cfg = dec["cfg"]
@@ -393,6 +470,7 @@ def main():
         "window": win,
         "page_encode": penc,
         "per_group": pgr,
+        "tasq": tqr,
         "encode": enc,
     }
     print(json.dumps(line), flush=True)

@@ -263,6 +263,8 @@ int loopvq_encode_tasq(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   if (n_tok == 0) return LOOPVQ_OK;
   if (!xk || !xv || !slot_mapping || !workspace) return LOOPVQ_ERR_INVALID_ARG;
   if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  // the transform reads keys and weights in 16-byte runs
+  if (((uintptr_t)xk & 15) != 0 || ((uintptr_t)tasq->w & 15) != 0) return LOOPVQ_ERR_INVALID_ARG;
   if (workspace_bytes < loopvq_encode_tasq_workspace_bytes(dims, n_tok, n_blocks)) return LOOPVQ_ERR_WORKSPACE;
   // the rest of the checks are the encoder's, made before anything is launched
   if (!cb || !hsq || !index_cache || (n_blocks > 1 && block_stride_bytes <= 0)) return LOOPVQ_ERR_INVALID_ARG;

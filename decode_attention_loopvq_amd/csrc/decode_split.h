@@ -344,7 +344,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // the lane's two V positions
   // (TaSQ: also the fp16 sigma of the lane's two V positions, issued before
   // the V rows so that waiting for the rows covers them)
-  auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW], uint32_t* sg) {
+  auto row_load = [&](int st, const int* raw_page, uint32_t (*kw)[LW], uint32_t (*vw)[LW], uint32_t& sg) {
     const uint8_t* vbase;
     size_t vslot;                               // first slot of the V rows' group (page*P + offset)
     if constexpr (SP) {
@@ -373,9 +373,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       vslot = (size_t)page * P + (gs & (P - 1));
     }
     if constexpr (TQ) {
-      const uint16_t* sp = p.tq_sigma + vslot + la;
-      sg[0] = sp[0];
-      sg[1] = sp[4];
+      // both into one register (16-bit loads into its low and high halves)
+      const _Float16* sp = (const _Float16*)p.tq_sigma + vslot + la;
+      half2v hv;
+      hv.x = sp[0];
+      hv.y = sp[4];
+      sg = __builtin_bit_cast(uint32_t, hv);
     }
     RowLoad<LB>::load(vbase + vro, vw[0]);
     RowLoad<LB>::load(vbase + vro + 4 * R, vw[1]);
@@ -506,14 +509,14 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      lazy max) and the V side: acc += p * v on the matrix cores (block =
   //      one token); p is rounded to fp16 for the product, and l adds the same
   //      rounded p, so the output stays an exact convex combination
-  auto v_side = [&](int g0, const float* sv2, const uint32_t* sg) {
+  auto v_side = [&](int g0, const float* sv2, uint32_t sg) {
     const int posa = g0 + vrel;
     const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 4) < vspan;
     float s0 = sv2[0], s1 = sv2[1];
     if constexpr (TQ) {
       // the rebuilt key is sigma * P^-1(u_hat) / w: the score scales by sigma
-      s0 *= (float)__builtin_bit_cast(_Float16, (uint16_t)sg[0]);
-      s1 *= (float)__builtin_bit_cast(_Float16, (uint16_t)sg[1]);
+      s0 *= (float)as_h2(sg).x;
+      s1 *= (float)as_h2(sg).y;
     }
     const float sa = va ? s0 * p.scale_log2 : -INFINITY;
     const float sb = vb ? s1 * p.scale_log2 : -INFINITY;
@@ -585,8 +588,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       // (page ids pgr, read two steps earlier) and reads the pages of st+5.
       // (TaSQ: sigma of a step travels with its index rows, and moves to sgc
       // when the step's V entries are gathered, before the rows are refilled)
-      uint32_t sgc[2] = {0u, 0u};
-      auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], uint32_t* sgn, int* pgr) {
+      uint32_t sgc = 0u;
+      auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], uint32_t& sgn, int* pgr) {
         float sc[2], sv2[2];
         k_side(sc);
         table_load(st + 1);                             // RoPE rows of step st+1
@@ -594,12 +597,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         gather_k(kwn);                                  // K entries of step st+1
         v_side(p0 + st * NT, sv2, sgc);
         gather_v(vwn);                                  // V entries of step st+1
-        if constexpr (TQ) { sgc[0] = sgn[0]; sgc[1] = sgn[1]; }
+        if constexpr (TQ) sgc = sgn;
         row_load(st + 3, pgr, kwn, vwn, sgn);
         page_at(st + 5, pgr);
       };
       uint32_t kwA[NS][LW], vwA[2][LW], kwB[NS][LW], vwB[2][LW];
-      uint32_t sgA[2], sgB[2];
+      uint32_t sgA = 0u, sgB = 0u;
       int pgA[NPG], pgB[NPG], pg0[NPG];
       page_at(0, pg0);
       row_load(0, pg0, kwA, vwA, sgA);
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       table_load(0);
       gather_k(kwA);
       gather_v(vwA);
-      if constexpr (TQ) { sgc[0] = sgA[0]; sgc[1] = sgA[1]; }
+      if constexpr (TQ) sgc = sgA;
       page_at(2, pg0);
       row_load(2, pg0, kwA, vwA, sgA);
       page_at(3, pgB);
@@ -699,7 +702,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       for (int s = 0; s < NS; ++s)
         pg[s] = plist[s * PGMAX + min((min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
     };
-    uint32_t kw[4][NS][LW], vw[4][2][LW], sg[4][2];
+    uint32_t kw[4][NS][LW], vw[4][2][LW], sg[4] = {0u, 0u, 0u, 0u};
     int pgn[NS];                             // page ids of step st+3, read during step st-1
     // one step: index rows of step x live in row buffer x % 4, staged pieces
     // alternate with b2 = st % 2.  Every global load of a step (staged rows,

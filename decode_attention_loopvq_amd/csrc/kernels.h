@@ -88,6 +88,7 @@ struct TasqParams {
   int64_t sigma_stride;
   float* u;                   // [n_steps][n_tok][H][D] fp32
   int n_tok, H, D, Tc, first_step;
+  int n_steps;                // loop steps of this call (set by the launcher)
 };
 
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,

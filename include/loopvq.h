@@ -341,8 +341,9 @@ size_t loopvq_encode_tasq_workspace_bytes(const loopvq_dims* dims, int32_t n_tok
  * loopvq_encode with TaSQ-coded keys: computes sigma (stored at each token's
  * slot for every coded loop step) and u, then codes u as the keys and xv as
  * the values.  Arguments as for loopvq_encode; xk holds the pre-RoPE keys.
- * workspace: at least loopvq_encode_tasq_workspace_bytes(dims, n_tok,
- * n_blocks) bytes, 256-byte aligned.  The key codes differ from an exact
+ * xk and tasq->w must be 16-byte aligned.  workspace: at least
+ * loopvq_encode_tasq_workspace_bytes(dims, n_tok, n_blocks) bytes, 256-byte
+ * aligned.  The key codes differ from an exact
  * evaluation only where two distances lie within fp32 rounding of each other
  * (u is formed in fp64 and rounded once to fp32), and sigma only where the
  * exact RMS lies within fp64 rounding of an fp16 rounding midpoint.

@@ -186,6 +186,8 @@ def test_tasq_validation_before_launch(L):
         assert enc(tq=bad) == -1
     assert enc(ws=ws_enc - 1) == -3
     assert enc(work=ctypes.c_void_p(F + 16)) == -1            # workspace not 256-byte aligned
+    assert enc(ptr=ctypes.c_void_p(F + 8)) == -1              # keys not 16-byte aligned
+    assert enc(tq=L.loopvq_tasq(F + 4, F, F, 4096)) == -1     # weights not 16-byte aligned
     assert enc(ptr=None) == -1
     assert enc(n_tok=-1) == -1
     assert enc(nb=2) == -1
