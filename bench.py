@@ -13,8 +13,9 @@ are reported beside the headline: the same batch with a 64-token bf16 sink
 and a 256-token bf16 recent window ("window"), the decode-time coding of
 one 8-token window page per request ("page_encode"), the split pass with one
 codebook per channel group ("per_group"), TaSQ-coded keys on the same batch
-and the TaSQ transform + coding of the prefill ("tasq"), and the encoder on
-the prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode").
+and the TaSQ transform + coding of the prefill ("tasq"), the encoder on the
+prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode"), and one
+k-means Lloyd iteration over that prefill's coupled vectors ("kmeans").
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -309,6 +310,57 @@ def bench_tasq(args, torch, np, synth, lv, dec):
     return res
 
 
+def bench_kmeans(args, torch, np, synth, lv):
+    """One Lloyd iteration of plain k-means over the coupled vectors of the 1.4B-layer
+    prefill (8 x 4096 tokens, 16 KV heads, K and V): assignment by the encoder, then the
+    codebook update."""
+    cfg = synth.config_by_name("layer1p4b")
+    n_tok = cfg.encode_batch * cfg.encode_tokens
+    lens = np.full(cfg.encode_batch, cfg.encode_tokens)
+    bt_np, num_pages = synth.make_block_table(cfg, lens)
+    slots = torch.from_numpy(np.concatenate([synth.slot_mapping_for(bt_np, b, int(n), cfg.page_size)
+                                             for b, n in enumerate(lens)])).cuda()
+    dims = lv.loopvq_dims.make(D=cfg.D, c=cfg.c, Tc=cfg.Tc, T=cfg.T, bits=cfg.bits, H_kv=cfg.H_kv,
+                               H_q=cfg.H_q, page_size=cfg.page_size, x_dtype=cfg.x_dtype,
+                               io_dtype=cfg.io_dtype)
+    cb = torch.from_numpy(synth.make_codebooks(cfg)).cuda()
+    cb2 = torch.empty_like(cb)
+    err = torch.zeros((cfg.n_blocks, cfg.H_kv, 2, 2), dtype=torch.float64, device="cuda")
+    wsk = torch.empty(lv.loopvq_kmeans_workspace_bytes(dims, cfg.n_blocks), dtype=torch.uint8, device="cuda")
+    xk, xv = synth.make_kv_torch(cfg, n_tok, 79)
+    cache = torch.zeros((num_pages, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+    _, hsq = lv.loopvq_build_codebook_slices(dims, cb)
+
+    def iteration(src, dst):
+        lv.loopvq_build_codebook_slices(dims, src, hsq=hsq, slices=slices_buf)
+        lv.loopvq_encode(dims, xk, xv, src, hsq, slots, cache)
+        lv.loopvq_kmeans_update(dims, xk, xv, slots, cache, src, cb_out=dst, err=err, workspace=wsk)
+    slices_buf = torch.empty((cfg.T, cfg.H_kv, 2, cfg.K, cfg.c), dtype=torch.float16, device="cuda")
+    iteration(cb, cb2)
+    iteration(cb2, cb)
+    torch.cuda.synchronize()
+    reps = max(3, args.steps // 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eu0, eu1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        iteration(cb if i % 2 == 0 else cb2, cb2 if i % 2 == 0 else cb)
+    e1.record()
+    eu0.record()
+    lv.loopvq_kmeans_update(dims, xk, xv, slots, cache, cb, cb_out=cb2, err=err, workspace=wsk)
+    eu1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    vecs = n_tok * cfg.H_kv * 2 * cfg.n_groups * cfg.n_blocks
+    e = err.cpu().numpy()
+    del xk, xv
+    return {"metric": "k-means Lloyd iterations/s", "value": round(1e3 / ms, 2), "unit": "iterations/s",
+            "ms_per_iteration": round(ms, 4), "update_ms": round(eu0.elapsed_time(eu1), 4),
+            "workload": f"{cfg.name}: {vecs} coupled vectors (8 x 4096 tokens, H_kv={cfg.H_kv}, K and V, G={cfg.G}), "
+                        f"K={cfg.K}: slices + assignment (encoder) + codebook update",
+            "nmse_after": round(float(e[..., 0].sum() / e[..., 1].sum()), 5)}
+
+
 def bench_page_encode(args, torch, np, synth, lv, dec):
     """Decode-time page encoding at the 32K batch's shape: the oldest 8-token bf16
     window page of each of the 16 requests, coded for all loop steps at once."""
@@ -442,6 +494,7 @@ def main():
     pgr = bench_per_group(args, torch, np, synth, lv, dec)
     tqr = bench_tasq(args, torch, np, synth, lv, dec)
     enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
+    kms = None if args.skip_encode else bench_kmeans(args, torch, np, synth, lv)
     cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
     cfg = dec["cfg"]
     line = {
@@ -472,6 +525,7 @@ def main():
         "per_group": pgr,
         "tasq": tqr,
         "encode": enc,
+        "kmeans": kms,
     }
     print(json.dumps(line), flush=True)
 

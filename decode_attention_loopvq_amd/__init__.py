@@ -10,4 +10,5 @@ from ._lib import (  # noqa: F401
     loopvq_encode, loopvq_decode_workspace_bytes, loopvq_decode_attn, loopvq_decode_split,
     loopvq_decode_combine, loopvq_bf16_window, loopvq_decode_attn_window, loopvq_encode_pages,
     loopvq_tasq, loopvq_encode_tasq_workspace_bytes, loopvq_encode_tasq, loopvq_decode_attn_tasq,
+    loopvq_kmeans_workspace_bytes, loopvq_kmeans_update,
 )

@@ -116,6 +116,10 @@ def lib() -> ctypes.CDLL:
         L.loopvq_decode_attn_tasq.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.POINTER(loopvq_tasq),
                                               ctypes.POINTER(loopvq_bf16_window), ctypes.c_float,
                                               P, P, P, ctypes.c_size_t, P]
+        L.loopvq_kmeans_workspace_bytes.restype = ctypes.c_size_t
+        L.loopvq_kmeans_workspace_bytes.argtypes = [D, I]
+        L.loopvq_kmeans_update.restype = ctypes.c_int
+        L.loopvq_kmeans_update.argtypes = [D, I, I, I, P, P, P, P, ctypes.c_int64, P, P, P, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -125,7 +129,7 @@ EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_s
             "loopvq_decode_workspace_bytes",
             "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine",
             "loopvq_decode_attn_window", "loopvq_encode_tasq_workspace_bytes", "loopvq_encode_tasq",
-            "loopvq_decode_attn_tasq")
+            "loopvq_decode_attn_tasq", "loopvq_kmeans_workspace_bytes", "loopvq_kmeans_update")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -410,3 +414,38 @@ def loopvq_decode_attn_tasq(dims: loopvq_dims, t: int, q: torch.Tensor, index_ca
                                          _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()),
                                          _stream()), "loopvq_decode_attn_tasq")
     return out, lse
+
+
+def loopvq_kmeans_workspace_bytes(dims: loopvq_dims, n_blocks: int) -> int:
+    return int(lib().loopvq_kmeans_workspace_bytes(ctypes.byref(dims), int(n_blocks)))
+
+
+def loopvq_kmeans_update(dims: loopvq_dims, xk: torch.Tensor, xv: torch.Tensor, slot_mapping: torch.Tensor,
+                         index_cache: torch.Tensor, cb: torch.Tensor, cb_out: Optional[torch.Tensor] = None,
+                         err: Optional[torch.Tensor] = None, first_block: int = 0, n_blocks: Optional[int] = None,
+                         block_stride_bytes: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
+    """Codebook half of a Lloyd iteration after loopvq_encode assigned the codes; returns (cb_out, err)."""
+    xdt = torch.float32 if dims.x_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+    _need(xk, xdt, "xk"); _need(xv, xdt, "xv"); _need(cb, torch.float16, "cb")
+    _need(slot_mapping, torch.int32, "slot_mapping"); _need(index_cache, torch.uint8, "index_cache")
+    if n_blocks is None:
+        n_blocks = xk.shape[0] // dims.Tc
+    n_tok = xk.shape[1]
+    if xk.shape != xv.shape or xk.shape[0] != n_blocks * dims.Tc or slot_mapping.numel() != n_tok:
+        raise ValueError("kmeans_update: inconsistent shapes")
+    if block_stride_bytes is None:
+        block_stride_bytes = index_cache.numel() // max(n_blocks, 1) if n_blocks > 1 else 0
+    if cb_out is None:
+        cb_out = torch.empty_like(cb)
+    _need(cb_out, torch.float16, "cb_out")
+    if err is None:
+        err = torch.zeros((dims.n_blocks, dims.H_kv, 2, 2), dtype=torch.float64, device=cb.device)
+    _need(err, torch.float64, "err")
+    need = loopvq_kmeans_workspace_bytes(dims, n_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=cb.device)
+    _check(lib().loopvq_kmeans_update(ctypes.byref(dims), n_tok, first_block, n_blocks, _ptr(xk), _ptr(xv),
+                                      _ptr(slot_mapping), _ptr(index_cache), int(block_stride_bytes), _ptr(cb),
+                                      _ptr(cb_out), _ptr(err), _ptr(workspace), int(workspace.numel()), _stream()),
+           "loopvq_kmeans_update")
+    return cb_out, err

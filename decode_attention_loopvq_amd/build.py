@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libloopvq.so")
-SOURCES = ["abi.hip", "decode.hip", "decode_pg.hip", "decode_tasq.hip", "encode.hip", "tasq.hip", "window.hip"]
+SOURCES = ["abi.hip", "decode.hip", "decode_pg.hip", "decode_tasq.hip", "encode.hip", "kmeans.hip", "tasq.hip", "window.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

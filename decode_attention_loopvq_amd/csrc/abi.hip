@@ -31,7 +31,9 @@ int check_dims(const loopvq_dims* d) {
     return LOOPVQ_ERR_INVALID_ARG;
   if (d->bits != 4 && d->bits != 8) return LOOPVQ_ERR_UNSUPPORTED;
   if (d->D != 64 && d->D != 128) return LOOPVQ_ERR_UNSUPPORTED;
-  if (d->c != 2 && d->c != 4 && d->c != 8) return LOOPVQ_ERR_UNSUPPORTED;
+  // c = 16 (with Tc = 1) is encoder-only: G channels of one step, the baseline grouping
+  if (d->c != 2 && d->c != 4 && d->c != 8 && d->c != 16) return LOOPVQ_ERR_UNSUPPORTED;
+  if (d->c == 16 && d->Tc != 1) return LOOPVQ_ERR_UNSUPPORTED;
   if ((d->D / d->c) % 8 != 0) return LOOPVQ_ERR_UNSUPPORTED;
   const int G = d->c * d->Tc;
   if (G != 8 && G != 16 && G != 32) return LOOPVQ_ERR_UNSUPPORTED;
@@ -178,7 +180,8 @@ static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   if (n_tok < 0 || first_block < 0 || n_blocks < 1 || first_block + n_blocks > nb_total)
     return LOOPVQ_ERR_INVALID_ARG;
   if (n_blocks > 1 && block_stride_bytes <= 0) return LOOPVQ_ERR_INVALID_ARG;
-  if ((dims->D / dims->c) % 16 != 0) return LOOPVQ_ERR_UNSUPPORTED;
+  // 4-bit rows pack the codes of groups g, g^1 into one byte: 16 groups or more
+  if ((dims->D / dims->c) % (dims->bits == 4 ? 16 : 8) != 0) return LOOPVQ_ERR_UNSUPPORTED;
   if (n_tok == 0) return LOOPVQ_OK;
   if (!xk || !xv || !cb || !hsq || !slot_mapping || !index_cache) return LOOPVQ_ERR_INVALID_ARG;
   const int H = dims->H_kv, K = dims->K * n_codebook_groups(dims), G = dims->c * dims->Tc;
@@ -268,7 +271,7 @@ int loopvq_encode_tasq(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   if (workspace_bytes < loopvq_encode_tasq_workspace_bytes(dims, n_tok, n_blocks)) return LOOPVQ_ERR_WORKSPACE;
   // the rest of the checks are the encoder's, made before anything is launched
   if (!cb || !hsq || !index_cache || (n_blocks > 1 && block_stride_bytes <= 0)) return LOOPVQ_ERR_INVALID_ARG;
-  if ((dims->D / dims->c) % 16 != 0) return LOOPVQ_ERR_UNSUPPORTED;
+  if ((dims->D / dims->c) % (dims->bits == 4 ? 16 : 8) != 0) return LOOPVQ_ERR_UNSUPPORTED;
   TasqParams tp{};
   tp.xk = xk;
   tp.w = tasq->w;
@@ -291,6 +294,52 @@ int loopvq_encode_tasq(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   if (st != LOOPVQ_OK) return st;
   return encode_impl(dims, n_tok, first_block, n_blocks, xv, xv, nullptr, step_stride, cb, hsq, slot_mapping,
                      index_cache, block_stride_bytes, 1, 1, dims->x_dtype == LOOPVQ_DTYPE_F32, stream);
+}
+
+size_t loopvq_kmeans_workspace_bytes(const loopvq_dims* dims, int32_t n_blocks) {
+  if (check_dims(dims) != LOOPVQ_OK || n_blocks < 0) return 0;
+  const size_t per = (size_t)dims->K * dims->c * dims->Tc + dims->K + 2;
+  return align256((size_t)n_blocks * 2 * dims->H_kv * per * sizeof(double));
+}
+
+int loopvq_kmeans_update(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
+                         const void* xk, const void* xv, const int32_t* slot_mapping, const uint8_t* index_cache,
+                         int64_t block_stride_bytes, const void* cb, void* cb_out, double* err, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != LOOPVQ_OK) return st;
+  if (dims->per_group) return LOOPVQ_ERR_UNSUPPORTED;
+  const int nb_total = dims->T / dims->Tc;
+  if (n_tok < 0 || first_block < 0 || n_blocks < 1 || first_block + n_blocks > nb_total)
+    return LOOPVQ_ERR_INVALID_ARG;
+  if (n_blocks > 1 && block_stride_bytes <= 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (!cb || !cb_out || !workspace) return LOOPVQ_ERR_INVALID_ARG;
+  if (n_tok > 0 && (!xk || !xv || !slot_mapping || !index_cache)) return LOOPVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return LOOPVQ_ERR_INVALID_ARG;
+  if (workspace_bytes < loopvq_kmeans_workspace_bytes(dims, n_blocks)) return LOOPVQ_ERR_WORKSPACE;
+  const int H = dims->H_kv, K = dims->K, G = dims->c * dims->Tc;
+  KmeansParams p{};
+  p.xk = xk;
+  p.xv = xv;
+  p.slot_mapping = slot_mapping;
+  p.cache = index_cache;
+  p.block_stride = block_stride_bytes;
+  p.cb = (const uint16_t*)cb + (size_t)first_block * H * 2 * K * G;
+  p.cb_out = (uint16_t*)cb_out + (size_t)first_block * H * 2 * K * G;
+  p.err = err;
+  p.gsum = (double*)workspace;
+  p.n_tok = n_tok;
+  p.H_kv = H;
+  p.D = dims->D;
+  p.c = dims->c;
+  p.Tc = dims->Tc;
+  p.K = K;
+  p.bits = dims->bits;
+  p.log2P = ilog2(dims->page_size);
+  // about 2048 workgroups over the call
+  const long long streams = (long long)n_blocks * 2 * H;
+  p.tok_per_wg = (int)std::max<long long>(16, ((long long)n_tok * streams + 2047) / 2048);
+  return hip_status(launch_kmeans_update(dims->x_dtype == LOOPVQ_DTYPE_F32, p, n_blocks, stream));
 }
 
 size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B, int32_t max_seq_len) {

@@ -315,6 +315,8 @@ hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int 
   LVQ_ENC_C(16, false, 8) LVQ_ENC_C(32, false, 8) LVQ_ENC_C(16, false, 4) LVQ_ENC_C(32, false, 4)
   LVQ_ENC_C(8, true, 8) LVQ_ENC_C(16, true, 8) LVQ_ENC_C(32, true, 8)
   LVQ_ENC_C(8, true, 4) LVQ_ENC_C(16, true, 4) LVQ_ENC_C(32, true, 4)
+  // G channels of one loop step (c = G, Tc = 1): the baseline grouping
+  LVQ_ENC(16, 16, false, 8) LVQ_ENC(16, 16, true, 8)
 #undef LVQ_ENC_C
 #undef LVQ_ENC
   return hipErrorInvalidValue;

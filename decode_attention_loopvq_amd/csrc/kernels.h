@@ -91,6 +91,21 @@ struct TasqParams {
   int n_steps;                // loop steps of this call (set by the launcher)
 };
 
+// codebook update of one Lloyd iteration (the codes come from the encoder)
+struct KmeansParams {
+  const void* xk;             // [n_blocks*Tc][n_tok][H_kv][D], bf16 or fp32
+  const void* xv;
+  const int32_t* slot_mapping;
+  const uint8_t* cache;       // index cache of the first block
+  int64_t block_stride;
+  const uint16_t* cb;         // [n_blocks][H_kv][2][K][G] fp16 codebooks that assigned the codes
+  uint16_t* cb_out;           // updated codebooks, same layout
+  double* err;                // [n_blocks][H_kv][2][2]: sum ||z - e||^2, sum ||z||^2, or null
+  double* gsum;               // workspace: per stream [K][G] sums, [K] counts, 2 error sums
+  int n_tok, H_kv, D, c, Tc, K, bits, log2P;
+  int tok_per_wg;
+};
+
 hipError_t launch_decode_split(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
                                hipStream_t s);
 hipError_t launch_decode_split_pg(int D, int C, int bits, bool qf32, const DecodeParams& p, int grid,
@@ -101,6 +116,7 @@ hipError_t launch_decode_combine(int D, bool out_bf16, const CombineParams& p, h
 hipError_t launch_decode_window(int D, bool qf32, const WindowParams& p, int B, hipStream_t s);
 hipError_t launch_encode(int G, bool xf32, int bits, const EncodeParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_tasq_transform(bool xf32, const TasqParams& p, int n_steps, hipStream_t s);
+hipError_t launch_kmeans_update(bool xf32, const KmeansParams& p, int n_blocks, hipStream_t s);
 hipError_t launch_build_slices(const uint16_t* cb, uint16_t* slices, float* hsq, int n_blocks, int H_kv,
                                int K, int c, int Tc, hipStream_t s);
 

@@ -76,7 +76,8 @@ enum { LOOPVQ_DTYPE_F32 = 0, LOOPVQ_DTYPE_BF16 = 1 };
 
 typedef struct loopvq_dims {
   int32_t D;          /* head dimension: 64 or 128                                      */
-  int32_t c;          /* channels per loop step covered by one code: 2, 4 or 8          */
+  int32_t c;          /* channels per loop step covered by one code: 2, 4 or 8 (16 with
+                         Tc = 1: G channels of one step, for the encoder and k-means only) */
   int32_t Tc;         /* loop steps per block (one code serves Tc steps); Tc | T        */
   int32_t T;          /* loop steps                                                     */
   int32_t bits;       /* code width: 4 or 8                                             */
@@ -90,9 +91,9 @@ typedef struct loopvq_dims {
                          channel groups; 1: one codebook per channel group as well
                          (8-bit codes only)                                             */
 } loopvq_dims;
-/* Supported shapes: D in {64, 128}; D/c a multiple of 8; G = c*Tc in {8, 16, 32}
- * (G = 8 only with fp32 encoder input); 4-bit codes only with K = 16 and
- * 8-bit only with K = 256. */
+/* Supported shapes: D in {64, 128}; D/c a multiple of 8 (of 16 for the encoder
+ * with 4-bit codes); G = c*Tc in {8, 16, 32} (G = 8 only with fp32 encoder
+ * input); 4-bit codes only with K = 16 and 8-bit only with K = 256. */
 
 /* Human-readable text of a status code.  Never NULL. */
 const char* loopvq_status_string(int status);
@@ -371,6 +372,34 @@ int loopvq_decode_attn_tasq(const loopvq_dims* dims, int32_t t, int32_t B,
                             const loopvq_bf16_window* window, float sm_scale,
                             void* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Plain k-means on the coupled vectors of a layer, one Lloyd iteration per
+ * pair of calls: loopvq_encode assigns every coupled vector to its nearest
+ * entry (the codes it writes), then loopvq_kmeans_update moves each entry to
+ * the mean of the vectors coded with it.  [LoopVQ paper, section "Redundancy
+ * along the loop axis", Fig. 2c: unweighted k-means under the loop-axis
+ * grouping and under G channels of one step (c = G, Tc = 1 on the steps laid
+ * end to end as tokens), same bit width and number of codebooks.]
+ * The means are exact fp64 sums of the vectors divided by their count,
+ * rounded to fp16 (round to nearest even); an entry no vector uses keeps its
+ * value.  Arguments as for loopvq_encode (the same xk, xv, slot_mapping and
+ * index cache the assigning call used), plus:
+ *   cb        codebooks that assigned the codes (of blocks first_block ..),
+ *   cb_out    the updated codebooks, same layout (may not alias cb),
+ *   err       [n_blocks][H_kv][2][2] fp64 or NULL: sum over the coupled
+ *             vectors of ||z - e_code||^2 (e from cb) and of ||z||^2,
+ *   workspace loopvq_kmeans_workspace_bytes(dims, n_blocks) bytes, 256-byte
+ *             aligned.
+ * Requires per_group = 0.
+ */
+size_t loopvq_kmeans_workspace_bytes(const loopvq_dims* dims, int32_t n_blocks);
+int loopvq_kmeans_update(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
+                         int32_t n_blocks, const void* xk, const void* xv,
+                         const int32_t* slot_mapping, const uint8_t* index_cache,
+                         int64_t block_stride_bytes, const void* cb, void* cb_out,
+                         double* err, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -147,7 +147,7 @@ def test_encode_validation_before_launch(L):
     assert call(n_tok=0, ptr=None) == 0
     d8 = _dims(L, T=8)
     assert lib.loopvq_encode(ctypes.byref(d8), 4, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
-    d_small = _dims(L, D=64, c=8)          # 8 groups per token: encoder needs a multiple of 16
+    d_small = _dims(L, D=64, c=8, bits=4)  # 8 groups per token: 4-bit rows need a multiple of 16
     assert lib.loopvq_encode(ctypes.byref(d_small), 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
 
 
@@ -207,6 +207,31 @@ def test_tasq_validation_before_launch(L):
     assert dec(dims=_dims(L, bits=4)) == -2
     assert dec(win=L.loopvq_bf16_window(None, F, 4, F, F)) == -1
     assert dec(B=0) == 0
+
+
+def test_kmeans_validation_before_launch(L):
+    lib = L.lib()
+    d = _dims(L)
+    ws = L.loopvq_kmeans_workspace_bytes(d, 1)
+    assert ws == ((2 * 16 * (256 * 16 + 256 + 2) * 8 + 255) // 256) * 256
+    def call(n_tok=10, first=0, nb=1, ptr=FAKE, cb=FAKE, out=FAKE, work=FAKE, ws_bytes=ws, dims=d, stride=0):
+        return lib.loopvq_kmeans_update(ctypes.byref(dims), n_tok, first, nb, ptr, ptr, ptr, ptr, stride, cb, out,
+                                        None, work, ws_bytes, None)
+    assert call(n_tok=-1) == -1
+    assert call(nb=0) == -1 and call(first=1) == -1
+    assert call(ptr=None) == -1
+    assert call(cb=None) == -1 and call(out=None) == -1 and call(work=None) == -1
+    assert call(work=ctypes.c_void_p((1 << 20) + 64)) == -1
+    assert call(ws_bytes=ws - 1) == -3
+    assert call(dims=_dims(L, per_group=1)) == -2
+    d8 = _dims(L, T=8)
+    assert call(dims=d8, nb=2) == -1                    # two blocks need a block stride
+    # c = 16 at Tc = 1 (G channels of one step): encoder and k-means only
+    d16 = _dims(L, c=16, Tc=1)
+    assert L.loopvq_row_bytes(d16) == 8
+    assert lib.loopvq_decode_attn(ctypes.byref(d16), 1, 1, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 1, FAKE, 10, 0.0,
+                                  FAKE, None, FAKE, 1 << 20, None) == -2
+    assert lib.loopvq_row_bytes(ctypes.byref(_dims(L, c=16, Tc=2))) == -2
 
 
 def test_slices_validation(L):
