@@ -103,6 +103,8 @@ int check_tasq(const loopvq_dims* d, const loopvq_tasq* tq) {
   if (tq == nullptr || !tq->w || !tq->perm || !tq->sigma || tq->sigma_stride < 0) return LOOPVQ_ERR_INVALID_ARG;
   if (d->T > 1 && tq->sigma_stride == 0) return LOOPVQ_ERR_INVALID_ARG;
   if (d->bits != 8 || d->per_group) return LOOPVQ_ERR_UNSUPPORTED;
+  // the transform keeps the inverse pair permutation and one token's u row in 64 KiB of LDS
+  if ((long long)d->H_kv * d->D * 6 > 65536) return LOOPVQ_ERR_UNSUPPORTED;
   return LOOPVQ_OK;
 }
 

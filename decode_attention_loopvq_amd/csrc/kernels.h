@@ -88,7 +88,6 @@ struct TasqParams {
   int64_t sigma_stride;
   float* u;                   // [n_steps][n_tok][H][D] fp32
   int n_tok, H, D, Tc, first_step;
-  int n_steps;                // loop steps of this call (set by the launcher)
 };
 
 // codebook update of one Lloyd iteration (the codes come from the encoder)

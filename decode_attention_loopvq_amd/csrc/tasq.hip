@@ -11,15 +11,16 @@
 // covers c/2 whole RoPE pairs.  The coupled vectors of the keys are then built
 // from u as they would be from k.  A token whose fp16 sigma is 0 gets u = 0.
 //
-// MI355X mapping: one wave per (token, loop step), four per workgroup.  The
-// wave reads the token's H*D inputs in 16-byte runs, sums the weighted squares
-// in fp64 (the sum then matches an exact evaluation except within fp64
-// rounding of an fp16 rounding midpoint) and reduces across lanes with
-// shuffles; every lane then holds sigma.  u is formed in fp64 as w k * (1 /
-// sigma) and rounded to fp32; each lane writes 8 consecutive u channels (4
-// RoPE pairs of one head) as two 16-byte stores, reading their inputs at the
-// permuted positions (cached: the wave has just read the token's row).  The
-// pass is bound by HBM bandwidth (6 bytes per bf16 element).
+// MI355X mapping: one wave per (token, loop step), up to four tokens of one
+// step per workgroup.  The workgroup first inverts the block's pair
+// permutation into LDS.  The wave reads the token's H*D keys and weights in
+// 16-byte runs, sums the weighted squares in fp64 (the sum then matches an
+// exact evaluation except within fp64 rounding of an fp16 rounding midpoint)
+// and reduces across lanes with shuffles; every lane then holds sigma.  A
+// second pass over the same runs (cached) forms u = w k * (1 / sigma) in fp64,
+// rounds it once to fp32 and writes it to its u position in the wave's LDS
+// row; the row then goes out in 16-byte runs.  The pass is bound by HBM
+// bandwidth (6 bytes per bf16 element).
 #include <math.h>
 
 #include "common.h"
@@ -34,33 +35,46 @@ __device__ __forceinline__ double load_x(const void* x, size_t i) {
 }
 
 template <bool XF32>
+__device__ __forceinline__ void load_run(const void* x, size_t off, float* v) {
+  if constexpr (XF32) {
+    const float4v a = *(const float4v*)((const float*)x + off);
+    const float4v b = *(const float4v*)((const float*)x + off + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4v a = *(const uint4v*)((const uint16_t*)x + off);
+    const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16lo(wd[i]); v[2 * i + 1] = bf16hi(wd[i]); }
+  }
+}
+
+template <bool XF32>
 __global__ __launch_bounds__(256) void tasq_transform_kernel(TasqParams p) {
-  const int lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);   // token-major within a step
-  if (item >= (long long)p.n_tok * p.n_steps) return;                      // whole waves exit together
-  const int s = (int)(item / p.n_tok), j = (int)(item - (long long)s * p.n_tok);
+  extern __shared__ int tsm[];                // [H][D/2] inverse pair permutation, then one u row per wave
+  const int s = blockIdx.y;
   const int step = p.first_step + s;
   const int D = p.D, D2 = p.D / 2, HD = p.H * p.D;
-  const float* w = p.w + (size_t)step * HD;
+  int* tinv = tsm;                            // u pair holding each RoPE frequency
   const int32_t* perm = p.perm + (size_t)(step / p.Tc) * p.H * D2;
+  for (int i = threadIdx.x; i < p.H * D2; i += blockDim.x) {
+    const int h = i / D2;
+    const int f = perm[i];
+    if ((unsigned)f < (unsigned)D2) tinv[h * D2 + f] = i - h * D2;   // out-of-range entries are ignored
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (j >= p.n_tok) return;                  // whole waves, after the only barrier
+  float* urow = (float*)(tsm + p.H * D2) + (size_t)wave * HD;
+  const float* w = p.w + (size_t)step * HD;
   const size_t xoff = ((size_t)s * p.n_tok + j) * HD;
 
   // sum of (w k)^2 over the token's H*D values, 8 consecutive values per lane and pass
   double acc = 0.0;
   for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-    float x[8];
-    if constexpr (XF32) {
-      const float4v a = *(const float4v*)((const float*)p.xk + xoff + e0);
-      const float4v b = *(const float4v*)((const float*)p.xk + xoff + e0 + 4);
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-      const uint4v a = *(const uint4v*)((const uint16_t*)p.xk + xoff + e0);
-      const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo(wd[i]); x[2 * i + 1] = bf16hi(wd[i]); }
-    }
-    const float4v wa = *(const float4v*)(w + e0), wb = *(const float4v*)(w + e0 + 4);
-    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    float x[8], wv[8];
+    load_run<XF32>(p.xk, xoff + e0, x);
+    load_run<true>(w, e0, wv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const double y = (double)x[i] * (double)wv[i];
@@ -73,31 +87,40 @@ __global__ __launch_bounds__(256) void tasq_transform_kernel(TasqParams p) {
   if (lane == 0) p.sigma[(size_t)step * p.sigma_stride + p.slot_mapping[j]] = __builtin_bit_cast(uint16_t, s16);
   const double inv = (float)s16 > 0.f ? 1.0 / (double)(float)s16 : 0.0;
 
-  // u channels e0 .. e0+7 (pairs (e0 % D)/2 .. +3 of head e0 / D)
+  // u: key channel f of head h (f < D/2 or its partner f + D/2) goes to u
+  // channel 2*inv[f] (or 2*inv[f] + 1) of that head, through the LDS row
   for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-    const int h = e0 / D, p0 = (e0 - h * D) >> 1;
-    float u[8];
+    float x[8], wv[8];
+    load_run<XF32>(p.xk, xoff + e0, x);
+    load_run<true>(w, e0, wv);
+    const int h = e0 / D, f0 = e0 - h * D;
+    const int side = f0 >= D2 ? 1 : 0, fq = f0 - side * D2;   // the 8 channels lie in one half
+    float* dst = urow + h * D + side;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int f = min(max(perm[h * D2 + p0 + r], 0), D2 - 1);
-      const int cf = h * D + f, ch = cf + D2;
-      u[2 * r] = (float)(load_x<XF32>(p.xk, xoff + cf) * (double)w[cf] * inv);
-      u[2 * r + 1] = (float)(load_x<XF32>(p.xk, xoff + ch) * (double)w[ch] * inv);
+    for (int i = 0; i < 8; ++i) {
+      const int pp = min(max(tinv[h * D2 + fq + i], 0), D2 - 1);
+      dst[2 * pp] = (float)((double)x[i] * (double)wv[i] * inv);
     }
-    float* dst = p.u + xoff + e0;
-    *(float4v*)dst = (float4v){u[0], u[1], u[2], u[3]};
-    *(float4v*)(dst + 4) = (float4v){u[4], u[5], u[6], u[7]};
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's row is in LDS
+  __asm__ __volatile__("" ::: "memory");
+  for (int e0 = lane * 8; e0 < HD; e0 += 512) {
+    const float4v a = *(const float4v*)(urow + e0), b = *(const float4v*)(urow + e0 + 4);
+    float* out = p.u + xoff + e0;
+    *(float4v*)out = a;
+    *(float4v*)(out + 4) = b;
   }
 }
 
 hipError_t launch_tasq_transform(bool xf32, const TasqParams& p, int n_steps, hipStream_t s) {
-  const long long items = (long long)p.n_tok * n_steps;
-  if (items == 0) return hipSuccess;
-  TasqParams q = p;
-  q.n_steps = n_steps;
-  const dim3 grid((unsigned)((items + 3) / 4));
-  if (xf32) hipLaunchKernelGGL(tasq_transform_kernel<true>, grid, dim3(256), 0, s, q);
-  else hipLaunchKernelGGL(tasq_transform_kernel<false>, grid, dim3(256), 0, s, q);
+  if (p.n_tok == 0 || n_steps == 0) return hipSuccess;
+  const int HD = p.H * p.D;
+  // four tokens per workgroup while their rows fit next to the permutation in 64 KiB
+  const int wpb = (size_t)4 * HD * 4 + (size_t)HD * 2 <= 65536 ? 4 : 1;
+  const dim3 grid((p.n_tok + wpb - 1) / wpb, n_steps);
+  const size_t lds = (size_t)wpb * HD * 4 + (size_t)HD * 2;
+  if (xf32) hipLaunchKernelGGL(tasq_transform_kernel<true>, grid, dim3(64 * wpb), lds, s, p);
+  else hipLaunchKernelGGL(tasq_transform_kernel<false>, grid, dim3(64 * wpb), lds, s, p);
   return hipGetLastError();
 }
 

@@ -193,6 +193,7 @@ def test_tasq_validation_before_launch(L):
     assert enc(nb=2) == -1
     assert enc(dims=_dims(L, bits=4)) == -2                   # TaSQ keys: 8-bit codes only
     assert enc(dims=_dims(L, per_group=1)) == -2
+    assert enc(dims=_dims(L, H_kv=128, H_q=128)) == -2       # the transform's LDS row: H_kv*D <= 10922
     assert enc(n_tok=0, ptr=None) == 0
     ws = L.loopvq_decode_workspace_bytes(d, 4, 1000)
     def dec(t=1, B=4, tq=good, ptr=FAKE, ws_bytes=ws, dims=d, win=None):
