@@ -101,6 +101,8 @@ int check_tasq(const loopvq_dims* d, const loopvq_tasq* tq) {
   int st = check_dims(d);
   if (st != LOOPVQ_OK) return st;
   if (tq == nullptr || !tq->w || !tq->perm || !tq->sigma || tq->sigma_stride < 0) return LOOPVQ_ERR_INVALID_ARG;
+  // decode reads the sigma of two adjacent slots as one 4-byte word
+  if (((uintptr_t)tq->sigma & 3) != 0 || (tq->sigma_stride & 1) != 0) return LOOPVQ_ERR_INVALID_ARG;
   if (d->T > 1 && tq->sigma_stride == 0) return LOOPVQ_ERR_INVALID_ARG;
   if (d->bits != 8 || d->per_group) return LOOPVQ_ERR_UNSUPPORTED;
   // the transform keeps the inverse pair permutation and one token's u row in 64 KiB of LDS

@@ -216,8 +216,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   const bool active = item_ok && p0 < lenx;   // wave-uniform
 
   // V role: rows 0-1 of the wave serve pair 0 and rows 2-3 pair 1; a lane
-  // takes position slot la of the step's groups 2*rp and 2*rp + 1 (positions
-  // 8*rp + la and 8*rp + 4 + la) and channel quarter lb
+  // takes the adjacent positions 8*rp + 2*la and 8*rp + 2*la + 1 of the step
+  // and channel quarter lb
   const int sv = row >> 1, rp = row & 1;
   float m = -INFINITY;                   // running max (log2 domain)
   float l = 0.f;                         // sum of the rounded p used in the products
@@ -295,10 +295,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   const uint32_t voff = PG ? (uint32_t)((N + lb * Q) * KENT * EB) : (uint32_t)(KENT * 256) + koff;
   const uint32_t asel0 = lb == 0 ? 0x0c0c0100u : (lb == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
   const uint32_t asel1 = lb == 2 ? 0x0c0c0100u : (lb == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
-  // K-role lanes holding my V positions: row 2*rp (+1), position slot la;
-  // quarters 2*sv, 2*sv + 1 expose pair sv's score after the quarter sum
-  const int bperm_a = ((32 * rp) | ((2 * sv + (lb & 1)) << 2) | la) << 2;
-  const int bperm_b = bperm_a + 64;
+  // K-role lanes holding my V positions 8*rp + 2*la (+1): row 2*rp + la/2,
+  // position slots 2*(la%2) (+1); quarters 2*sv, 2*sv + 1 expose pair sv's
+  // score after the quarter sum
+  const int bperm_a = ((16 * (2 * rp + (la >> 1))) | ((2 * sv + (lb & 1)) << 2) | (2 * (la & 1))) << 2;
+  const int bperm_b = bperm_a + 4;
   const int P = 1 << p.log2P;
   const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
   const size_t page_stride = (size_t)p.H_kv * 2 * kv_stride;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // its group: the whole step inside one page (SP), or the row's own 4
   // positions (pages of 8 positions)
   const uint32_t kro = (uint32_t)(((SP ? 4 * row : 0) + lb) * R + la * LB);
-  const uint32_t vro = kv_stride + (uint32_t)(((SP ? 8 * rp : 0) + la) * R + lb * LB);   // +4R: slot b
+  const uint32_t vro = kv_stride + (uint32_t)(((SP ? 8 * rp : 0) + 2 * la) * R + lb * LB);   // +R: slot b
   const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
   int lim[2], last[2];
   const int32_t* btb[2];
@@ -318,9 +319,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     btb[s] = p.block_table + (size_t)bq[s] * p.max_pages;
   }
   const int limx = max(lim[0], lim[1]);
-  // the V lane's positions 8*rp + la (+4) of a step, relative to lo, and the
+  // the V lane's positions 8*rp + 2*la (+1) of a step, relative to lo, and the
   // span [lo, lim) of coded positions in this chunk
-  const int vrel = 8 * rp + la - lo[sv];
+  const int vrel = 8 * rp + 2 * la - lo[sv];
   const uint32_t vspan = (uint32_t)max(lim[sv] - lo[sv], 0);
   const int glast = (max(last[0], last[1]) >> 4) << 4;   // last step-aligned group with data
   const int my_steps = active ? (limx - p0 + NT - 1) / NT : 0;   // wave-uniform
@@ -373,15 +374,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       vslot = (size_t)page * P + (gs & (P - 1));
     }
     if constexpr (TQ) {
-      // both into one register (16-bit loads into its low and high halves)
-      const _Float16* sp = (const _Float16*)p.tq_sigma + vslot + la;
-      half2v hv;
-      hv.x = sp[0];
-      hv.y = sp[4];
-      sg = __builtin_bit_cast(uint32_t, hv);
+      // the two positions are adjacent: one 4-byte load (the slot is even)
+      sg = *(const uint32_t*)(p.tq_sigma + vslot + 2 * la);
     }
     RowLoad<LB>::load(vbase + vro, vw[0]);
-    RowLoad<LB>::load(vbase + vro + 4 * R, vw[1]);
+    RowLoad<LB>::load(vbase + vro + R, vw[1]);
   };
   // table rows of positions 4g..4g+3 are interleaved: chunk j of quarter la
   // of position 4g + n sits at float4 ((g*FP + j)*4 + la)*4 + n, so the 16
@@ -511,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      rounded p, so the output stays an exact convex combination
   auto v_side = [&](int g0, const float* sv2, uint32_t sg) {
     const int posa = g0 + vrel;
-    const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 4) < vspan;
+    const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 1) < vspan;
     float s0 = sv2[0], s1 = sv2[1];
     if constexpr (TQ) {
       // the rebuilt key is sigma * P^-1(u_hat) / w: the score scales by sigma

@@ -322,7 +322,7 @@ int loopvq_decode_attn_window(const loopvq_dims* dims, int32_t t, int32_t B,
  *                 (page*P + offset) at sigma[t*sigma_stride + s].  Written by
  *                 loopvq_encode_tasq, read by loopvq_decode_attn_tasq.
  *   sigma_stride  elements between the arrays of consecutive loop steps
- *                 (> 0 when T > 1).
+ *                 (even; > 0 when T > 1).  sigma is 4-byte aligned.
  * TaSQ-coded keys need 8-bit codes, one codebook per (block, head, K|V)
  * (per_group = 0) and H_kv*D <= 10922; other shapes return
  * LOOPVQ_ERR_UNSUPPORTED.  The K codebooks are codebooks of u.

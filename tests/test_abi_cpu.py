@@ -182,7 +182,8 @@ def test_tasq_validation_before_launch(L):
                                       work, ws, None)
     assert enc(tq=None) == -1
     for bad in (L.loopvq_tasq(None, F, F, 4096), L.loopvq_tasq(F, None, F, 4096), L.loopvq_tasq(F, F, None, 4096),
-                L.loopvq_tasq(F, F, F, 0), L.loopvq_tasq(F, F, F, -1)):
+                L.loopvq_tasq(F, F, F, 0), L.loopvq_tasq(F, F, F, -1),
+                L.loopvq_tasq(F, F, F + 2, 4096), L.loopvq_tasq(F, F, F, 4097)):   # sigma alignment / odd stride
         assert enc(tq=bad) == -1
     assert enc(ws=ws_enc - 1) == -3
     assert enc(work=ctypes.c_void_p(F + 16)) == -1            # workspace not 256-byte aligned
