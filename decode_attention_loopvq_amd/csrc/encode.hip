@@ -52,30 +52,35 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   // rows 8q + 4h + s), the MFMA accumulator inputs; -inf on unused rows
   __shared__ __attribute__((aligned(16))) float hsl[NTILE * 2 * 16];
 
+  // work-item and workgroup ids from the hardware registers: this file is
+  // built with -mno-amdgpu-ieee, which keeps the device library's id queries
+  // from inlining (they would be calls returning per-lane values)
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int bidx = (int)__builtin_amdgcn_workgroup_id_x(), bidy = (int)__builtin_amdgcn_workgroup_id_y();
   const int H = p.H_kv, Tc = p.Tc, D = p.D;
   // y = ((beta*kv_n + kv - kv_lo)*H + hd)*NG + gq: with one codebook per channel group
   // (PG) a workgroup codes group gq only, with that group's codebook
   const int NG = PG ? D / C : 1;
-  const int gq = PG ? (int)blockIdx.y % NG : 0;
-  const int y = PG ? (int)blockIdx.y / NG : (int)blockIdx.y;
+  const int gq = PG ? bidy % NG : 0;
+  const int y = PG ? bidy / NG : bidy;
   const int hd = y % H, kv = p.kv_lo + (y / H) % p.kv_n, beta = y / (p.kv_n * H);
   const size_t cbi = ((size_t)(beta * H + hd) * 2 + kv) * NG + gq;   // codebook of this workgroup
 
   // ---- codebook of (beta, hd, kv), permuted to loop-major coordinates
   const uint16_t* cbsrc = p.cb + cbi * KENT * G;
-  for (int x = threadIdx.x; x < KENT * G; x += blockDim.x) {
+  for (int x = tid; x < KENT * G; x += 256) {
     const int e = x / G, kap = x - e * G;
     const int m = kap / C, i = kap - m * C;
     cbp[x] = cbsrc[(size_t)e * G + i * Tc + m];
   }
-  for (int x = threadIdx.x; x < NTILE * 32; x += blockDim.x) {
+  for (int x = tid; x < NTILE * 32; x += 256) {
     const int t = x >> 5, hh = (x >> 4) & 1, q = (x >> 2) & 3, sr = x & 3;
     const int e = 32 * t + 8 * q + 4 * hh + sr;
     hsl[x] = e < KENT ? -p.hsq[cbi * KENT + e] : -INFINITY;
   }
   __syncthreads();
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hf = lane >> 5, col = lane & 31;
 
   // ---- entry operands (rows = entries 32t + col, reduction chunk hf), held
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   const void* xsrc = kv ? p.xv : p.xk;
   const int nvec = PG ? p.n_tok : p.n_tok * n;   // vectors of this stream (PG: of group gq)
   const int nunit = (nvec + 31) >> 5;  // units of 32 vectors
-  const int u0 = (blockIdx.x * 4 + wave) * p.units_per_wave;
+  const int u0 = (bidx * 4 + wave) * p.units_per_wave;
   const int u1 = min(u0 + p.units_per_wave, nunit);
   if (u0 >= u1) return;                // no work (no barrier follows)
 
@@ -124,17 +129,28 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     }
   // raw input words of one unit (bf16 pairs or fp32), converted at use
   struct Raw { uint32_t w[NMF][NRUN][RW]; };
+  // dense input with n <= 32 groups per token: a unit is 32/n whole tokens and
+  // a lane keeps its group, so its offset advances by a wave-uniform step per
+  // unit (no per-lane multiplies); the last, partial unit takes the clamped path
+  const bool incr = !PAGED && !PG && ln <= 5;
+  const size_t lane_off0 = (size_t)(col >> (ln <= 5 ? ln : 0)) * H * D + (size_t)(col & (n - 1)) * C;
+  const size_t unit_step = (size_t)(32 >> (ln <= 5 ? ln : 0)) * H * D;
   auto load_raw = [&](int u, Raw& r) {
-    const int v = min(u * 32 + col, nvec - 1);     // clamped: loads stay in bounds
-    const int tok = PG ? v : v >> ln, g = PG ? gq : v & (n - 1);
-    size_t tbase;
-    if constexpr (PAGED) {
-      const int ss = p.src_slot[tok];
-      tbase = ((size_t)(ss >> 3) * H * 16 + (ss & 7)) * D;
+    size_t voff;
+    if (incr && u * 32 + 31 < nvec) {
+      voff = lane_off0 + (size_t)u * unit_step;
     } else {
-      tbase = (size_t)tok * H * D;
+      const int v = min(u * 32 + col, nvec - 1);     // clamped: loads stay in bounds
+      const int tok = PG ? v : v >> ln, g = PG ? gq : v & (n - 1);
+      size_t tbase;
+      if constexpr (PAGED) {
+        const int ss = p.src_slot[tok];
+        tbase = ((size_t)(ss >> 3) * H * 16 + (ss & 7)) * D;
+      } else {
+        tbase = (size_t)tok * H * D;
+      }
+      voff = tbase + (size_t)g * C;
     }
-    const size_t voff = tbase + (size_t)g * C;
 #pragma unroll
     for (int mu = 0; mu < NMF; ++mu)
 #pragma unroll
@@ -188,6 +204,9 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
         }
   };
 
+  // rows of this (block, head, K|V) stream: page q holds them at q*page_bytes
+  const size_t page_bytes = (size_t)H * 2 * P * R;
+  uint8_t* const head_rows = p.cache + (int64_t)beta * p.block_stride + (size_t)(hd * 2 + kv) * P * R;
   // row slot of group g (the row order of the cache; q = n/8 is a power of two)
   const int lq = __builtin_ctz(n >> 3), hgr = n >> 1;
   auto slot_of = [&](int g) {
@@ -261,8 +280,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       bidx = take ? oi : bidx;
     }
     // ---- write the code into its row slot
-    uint8_t* row = p.cache + (int64_t)beta * p.block_stride +
-                   ((((size_t)(slot >> p.log2P) * H + hd) * 2 + kv) * P + (slot & (P - 1))) * R;
+    uint8_t* row = head_rows + (size_t)(slot >> p.log2P) * page_bytes + (size_t)((slot & (P - 1)) * R);
     const int sl = slot_of(g);
     if constexpr (BITS == 8) {
       if (hf == 0 && vok) row[sl] = (uint8_t)bidx;
