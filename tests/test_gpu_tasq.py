@@ -145,6 +145,49 @@ def test_tasq_encode_then_decode():
         assert ratio <= 1.0
 
 
+def test_tasq_zero_keys_and_odd_token_counts():
+    # tokens whose keys are zero at some loop steps get sigma = 0 and u = 0 there;
+    # 37 tokens leave a partial workgroup of the transform and a partial encoder unit
+    cfg = synth.config_by_name("layer1p4b").replace(H_kv=2, H_q=2, n_calib=400)
+    n = 37
+    xk, xv = synth.make_kv(cfg, n, seed=190)
+    xk[1, 3] = 0.0
+    xk[:, 20] = 0.0
+    w, perm = synth.make_tasq(cfg)
+    u, s16 = tq.tasq_transform(xk, w, perm, cfg.Tc)
+    assert s16[1, 3] == 0 and np.all(s16[:, 20] == 0)
+    cb = _tasq_codebooks(cfg, w, perm, 191)
+    lens = np.array([n])
+    bt, npg = synth.make_block_table(cfg, lens)
+    P = cfg.page_size
+    slots = synth.slot_mapping_for(bt, 0, n, P)
+    layer = GpuLayer(cfg, cb, n)
+    cache = torch.zeros((npg, cfg.H_kv, 2, P, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+    sigma = torch.full((cfg.T, npg * P), 7.0, dtype=torch.float16, device="cuda")
+    lv.loopvq_encode_tasq(layer.dims, x_tensor(cfg, xk), x_tensor(cfg, xv), to_dev(w), to_dev(perm), sigma,
+                          layer.cb, layer.hsq, to_dev(slots), cache)
+    torch.cuda.synchronize()
+    got_sig = sigma.cpu().numpy().astype(np.float64)
+    exact = np.stack([tq.tasq_sigma(xk[t], w[t]) for t in range(cfg.T)])
+    mid = tq.f16_near_midpoint(exact)
+    assert np.array_equal(got_sig[:, slots][~mid], s16[~mid])
+    untouched = np.setdiff1d(np.arange(npg * P), slots)
+    assert np.all(got_sig[:, untouched] == 7.0)              # only the coded slots are written
+    ok = ~mid.any(axis=0)
+    ties, bad = check_codes(cfg, cache.cpu().numpy()[None], u[:, ok], xv[:, ok], cb, slots[ok])
+    assert bad == 0
+    ref_sigma = np.zeros((cfg.T, npg * P))
+    ref_sigma[:, slots] = s16
+    ref_cache, _, _ = oracle.build_index_cache(u, xv, cb, cfg.Tc, cfg.c, cfg.bits, slots, npg, P, method="gemm")
+    for t in (1, 2):
+        q = synth.make_queries(cfg, 1, t=t)
+        o, lse = layer.decode_tasq(t, q, to_dev(ref_cache[0]), bt, lens, w, perm, ref_sigma.astype(np.float16))
+        ref = ref_decode_tasq(cfg, t, q, ref_cache[0], bt, lens, cb, w, perm, ref_sigma)
+        err, ratio = compare(cfg, o, lse, ref, lens)
+        _note(f"zero-key tokens t={t}: max err {err:.2e}")
+        assert ratio <= 1.0
+
+
 @pytest.mark.parametrize("n_sink,n_recent", [(8, 64), (64, 256)])
 def test_tasq_decode_with_window(n_sink, n_recent):
     cfg = synth.config_by_name("layer1p4b")
