@@ -29,7 +29,7 @@ struct DecodeParams {
   int shared_rope;            // eight waves of a workgroup share a chunk and its RoPE rows
   int n_chunks;
   int items_per_head;         // n_dg * n_chunks wave work items per KV head
-  int wg_per_head;            // ceil(items_per_head / 4)
+  int wg_per_head;            // ceil(items_per_head / 8): eight waves per workgroup
   int max_seq_len;            // host bound; seq_lens are clamped to it
   float scale_log2;           // sm_scale * log2(e)
 };
