@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     // opaque per-unit base: keeps the accumulator-input reads inside the unit
     int hbase = hf * 64;
     __asm__ __volatile__("" : "+v"(hbase));
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) {
+    // scores of tile t: the MFMA with -0.5*||e||^2 as the accumulator input
+    auto tile_scores = [&](int t) {
       const uint8_t* hp = (const uint8_t*)hsl + t * 128 + hbase;
       const float4v c0 = *(const float4v*)hp, c1 = *(const float4v*)(hp + 16);
       const float4v c2 = *(const float4v*)(hp + 32), c3 = *(const float4v*)(hp + 48);
@@ -251,6 +251,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
                     c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
 #pragma unroll
       for (int mu = 0; mu < NMF; ++mu) d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[t][mu], Bv[mu], d, 0, 0, 0);
+      return d;
+    };
+    // the tile's maximum; a strictly larger one makes it the best tile
+    auto keep_best = [&](int t, const float16v& d) {
       float m = __builtin_fmaxf(__builtin_fmaxf(d[0], d[1]), d[2]);
       m = __builtin_fmaxf(__builtin_fmaxf(m, d[3]), d[4]);
       m = __builtin_fmaxf(__builtin_fmaxf(m, d[5]), d[6]);
@@ -259,14 +263,24 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       m = __builtin_fmaxf(__builtin_fmaxf(m, d[11]), d[12]);
       m = __builtin_fmaxf(__builtin_fmaxf(m, d[13]), d[14]);
       m = __builtin_fmaxf(m, d[15]);
-      // a new best tile is rare after the first few: a masked branch copies
-      // the scores (64-bit moves) instead of selecting all 16 every tile
+      // a masked branch copies the scores (64-bit moves) instead of selecting
+      // all 16 every tile; some lane of the wave takes it at almost every tile
       if (m > best) {
         __asm__ __volatile__("");          // keeps this a masked branch (no selects)
         best = m;
         btile = t;
         bd = d;
       }
+    };
+    // the MFMA of tile t+1 is issued before the search of tile t (whose
+    // masked branch ends a basic block), so the matrix core runs during it
+    float16v dc = tile_scores(0);
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      float16v dn;
+      if (t + 1 < NTILE) dn = tile_scores(t + 1);
+      keep_best(t, dc);
+      if (t + 1 < NTILE) dc = dn;
     }
     int rr = 15;
 #pragma unroll
