@@ -40,6 +40,9 @@ int check_dims(const loopvq_dims* d) {
   if (G == 8 && d->x_dtype != LOOPVQ_DTYPE_F32) return LOOPVQ_ERR_UNSUPPORTED;
   if (d->per_group != 0 && d->per_group != 1) return LOOPVQ_ERR_INVALID_ARG;
   if (d->per_group && d->bits != 8) return LOOPVQ_ERR_UNSUPPORTED;
+  // the kernels take the bytes of one index-cache page as a 32-bit value
+  const long long row_bytes = (long long)(d->D / d->c) * d->bits / 8;
+  if ((long long)d->H_kv * 2 * d->page_size * row_bytes > 0xffffffffLL) return LOOPVQ_ERR_UNSUPPORTED;
   return LOOPVQ_OK;
 }
 

@@ -302,7 +302,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   const int bperm_b = bperm_a + 4;
   const int P = 1 << p.log2P;
   const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
-  const size_t page_stride = (size_t)p.H_kv * 2 * kv_stride;
+  // bytes between pages (below 2^32: the boundary rejects larger strides), so
+  // a page's offset is one 32 x 32 -> 64-bit product of unsigned values
+  const uint32_t page_stride = (uint32_t)p.H_kv * 2u * kv_stride;
   const uint8_t* head_base = p.cache + (size_t)h * 2 * kv_stride;
   // byte offsets of the lane's K and V row quarters from the first row of
   // its group: the whole step inside one page (SP), or the row's own 4
@@ -353,10 +355,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       size_t slot0[2];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int page = has[s] ? __builtin_amdgcn_readfirstlane(raw_page[s]) : 0;
-        const int gs = min(p0 + st * NT, last[s]) & ~(NT - 1);
-        base[s] = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
-        slot0[s] = (size_t)page * P + (gs & (P - 1)) + 8 * rp;
+        const uint32_t page = has[s] ? (uint32_t)__builtin_amdgcn_readfirstlane(raw_page[s]) : 0u;
+        const uint32_t gs = (uint32_t)(min(p0 + st * NT, last[s]) & ~(NT - 1)) & (uint32_t)(P - 1);
+        base[s] = head_base + ((uint64_t)page * page_stride + gs * (uint32_t)R);
+        slot0[s] = (size_t)page * P + gs + 8 * rp;
         RowLoad<LB>::load(base[s] + kro, kw[s]);
       }
       vbase = (NS == 1 || sv == 0) ? base[0] : base[NS - 1];
@@ -364,14 +366,14 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     } else {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int page = has[s] ? raw_page[s] : 0;
-        const int gs = min(p0 + st * NT + 4 * row, last[s]) & ~3;
-        RowLoad<LB>::load(head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R + kro, kw[s]);
+        const uint32_t page = has[s] ? (uint32_t)raw_page[s] : 0u;
+        const uint32_t gs = (uint32_t)(min(p0 + st * NT + 4 * row, last[s]) & ~3) & (uint32_t)(P - 1);
+        RowLoad<LB>::load(head_base + ((uint64_t)page * page_stride + gs * (uint32_t)R) + kro, kw[s]);
       }
-      const int page = has[sv] ? raw_page[NS] : 0;
-      const int gs = min(p0 + st * NT + 8 * rp, last[sv]) & ~7;
-      vbase = head_base + (size_t)page * page_stride + (size_t)(gs & (P - 1)) * R;
-      vslot = (size_t)page * P + (gs & (P - 1));
+      const uint32_t page = has[sv] ? (uint32_t)raw_page[NS] : 0u;
+      const uint32_t gs = (uint32_t)(min(p0 + st * NT + 8 * rp, last[sv]) & ~7) & (uint32_t)(P - 1);
+      vbase = head_base + ((uint64_t)page * page_stride + gs * (uint32_t)R);
+      vslot = (size_t)page * P + gs;
     }
     if constexpr (TQ) {
       // the two positions are adjacent: one 4-byte load (the slot is even)
@@ -634,12 +636,17 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     // (read back per step with no long-lived registers): entry i of stream s
     // is the page of index pa[s] + i
     int* plist = (int*)(lds + LDS_SLICES + LDS_RING) + wave * 2 * PGMAX;
-    int pa[2], pcnt[2];
+    // the page of position x is list entry clamp(x, lo, last) / P - pa,
+    // capped at pcnt - 1; clamping commutes with the shift, so per step it is
+    // min(max(x / P - pa, plo), phi) with one shift shared by the streams
+    int pa[2], plo[2], phi[2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       pa[s] = min(max(p0, lo[s]), last[s]) >> p.log2P;
-      pcnt[s] = max(min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX), 1);
-      for (int i = lane; i < pcnt[s]; i += 64) plist[s * PGMAX + i] = has[s] ? btb[s][pa[s] + i] : 0;
+      const int pcnt = max(min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX), 1);
+      plo[s] = (lo[s] >> p.log2P) - pa[s];
+      phi[s] = min((last[s] >> p.log2P) - pa[s], pcnt - 1);
+      for (int i = lane; i < pcnt; i += 64) plist[s * PGMAX + i] = has[s] ? btb[s][pa[s] + i] : 0;
     }
     if (lane == 0) wsteps[wave] = my_steps;
     __syncthreads();
@@ -697,7 +704,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     auto page_lds = [&](int st, int* pg) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        pg[s] = plist[s * PGMAX + min((min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) - pa[s], pcnt[s] - 1)];
+        pg[s] = plist[s * PGMAX + min(max(((p0 + st * NT) >> p.log2P) - pa[s], plo[s]), phi[s])];
     };
     uint32_t kw[4][NS][LW], vw[4][2][LW], sg[4] = {0u, 0u, 0u, 0u};
     int pgn[NS];                             // page ids of step st+3, read during step st-1

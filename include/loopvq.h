@@ -40,7 +40,9 @@
  *   index cache      one cache per block beta: [num_pages][H_kv][2][P][R]
  *                    bytes, R = (D/c)*bits/8 bytes per row.  Page p holds the
  *                    rows of tokens p*P .. p*P+P-1 of whichever request maps
- *                    a logical page to it through its block table.
+ *                    a logical page to it through its block table.  One page
+ *                    (H_kv*2*P*R bytes) must be smaller than 4 GiB, else
+ *                    every entry point returns LOOPVQ_ERR_UNSUPPORTED.
  *   row order        A row stores the n = D/c codes of one token in the
  *                    "RoPE-pair interleaved" slot order: with h = n/2 and
  *                    q = n/8, slot s = i*2q + r (i < 4, r < 2q) holds group
