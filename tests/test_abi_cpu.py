@@ -64,7 +64,7 @@ def test_row_bytes(L):
     (dict(c=2, Tc=4), -2),                 # G = 8 needs fp32 encoder input
     (dict(x_dtype=7), -1),
     # one index-cache page (H_kv*2*P*R bytes) must stay below 4 GiB
-    (dict(H_kv=32768, H_q=32768, page_size=1024, c=2), -2),
+    (dict(H_kv=32768, H_q=32768, page_size=1024, c=2, x_dtype="f32"), -2),
 ])
 def test_invalid_dims(L, kw, status):
     assert L.lib().loopvq_row_bytes(ctypes.byref(_dims(L, **kw))) == status
@@ -72,7 +72,11 @@ def test_invalid_dims(L, kw, status):
 
 def test_large_page_accepted(L):
     # 1024 heads x 2 x 1024 positions x 64-byte rows: 128 MiB pages are fine
-    assert L.lib().loopvq_row_bytes(ctypes.byref(_dims(L, H_kv=1024, H_q=1024, page_size=1024, c=2))) == 64
+    d = _dims(L, H_kv=1024, H_q=1024, page_size=1024, c=2, x_dtype="f32")
+    assert L.lib().loopvq_row_bytes(ctypes.byref(d)) == 64
+    # the same shape with 32768 heads only fails on the page size
+    d = _dims(L, H_kv=32768, H_q=32768, page_size=512, c=2, x_dtype="f32")
+    assert L.lib().loopvq_row_bytes(ctypes.byref(d)) == 64
 
 
 def test_per_group_dims(L):
