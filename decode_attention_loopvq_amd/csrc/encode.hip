@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   const int n = D / C;                 // groups (vectors) per token, a power of two
   const int ln = __builtin_ctz(n);
   const int R = n * BITS / 8;
+  const int lr = __builtin_ctz(R);     // row bytes, a power of two
   const int P = 1 << p.log2P;
   const void* xsrc = kv ? p.xv : p.xk;
   const int nvec = PG ? p.n_tok : p.n_tok * n;   // vectors of this stream (PG: of group gq)
@@ -205,7 +206,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   };
 
   // rows of this (block, head, K|V) stream: page q holds them at q*page_bytes
-  const size_t page_bytes = (size_t)H * 2 * P * R;
+  // (below 2^32: the boundary rejects larger pages)
+  const uint32_t page_bytes = (uint32_t)H * 2u * (uint32_t)(P * R);
   uint8_t* const head_rows = p.cache + (int64_t)beta * p.block_stride + (size_t)(hd * 2 + kv) * P * R;
   // row slot of group g (the row order of the cache; q = n/8 is a power of two)
   const int lq = __builtin_ctz(n >> 3), hgr = n >> 1;
@@ -214,6 +216,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     const int gg = hi ? g - hgr : g;
     return ((gg >> lq) << (lq + 1)) + (hi ? (1 << lq) : 0) + (gg & ((1 << lq) - 1));
   };
+  // a lane's group is fixed when a unit holds whole tokens (n divides 32) or
+  // the workgroup codes one group (PG); then so is its row slot
+  const bool fixed_group = PG || ln <= 5;
+  const int sl_lane = slot_of(PG ? gq : (col & (n - 1)));
 
   // software pipeline over units: the raw loads of unit u+3 are issued while
   // unit u is scored
@@ -294,13 +300,17 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       bidx = take ? oi : bidx;
     }
     // ---- write the code into its row slot
-    uint8_t* row = head_rows + (size_t)(slot >> p.log2P) * page_bytes + (size_t)((slot & (P - 1)) * R);
-    const int sl = slot_of(g);
+    // byte of the code: page, row in the page (rows are a power of two of
+    // bytes), slot byte; unsigned 32-bit parts and one 32 x 32 -> 64 product
+    const uint32_t us = (uint32_t)slot;
+    const uint32_t sl = (uint32_t)(fixed_group ? sl_lane : slot_of(g));
+    uint8_t* const code = head_rows + ((uint64_t)(us >> p.log2P) * page_bytes +
+                                       (((us & (uint32_t)(P - 1)) << lr) + (BITS == 8 ? sl : sl >> 1)));
     if constexpr (BITS == 8) {
-      if (hf == 0 && vok) row[sl] = (uint8_t)bidx;
+      if (hf == 0 && vok) *code = (uint8_t)bidx;
     } else {
       const int other = __shfl_xor(bidx, 1);
-      if (hf == 0 && vok && (col & 1) == 0) row[sl >> 1] = (uint8_t)((bidx & 15) | ((other & 15) << 4));
+      if (hf == 0 && vok && (col & 1) == 0) *code = (uint8_t)((bidx & 15) | ((other & 15) << 4));
     }
   };
   int u = u0;
