@@ -17,10 +17,12 @@
 // 16-byte runs, sums the weighted squares in fp64 (the sum then matches an
 // exact evaluation except within fp64 rounding of an fp16 rounding midpoint)
 // and reduces across lanes with shuffles; every lane then holds sigma.  A
-// second pass over the same runs (cached) forms u = w k * (1 / sigma) in fp64,
+// second pass over the same values forms u = w k * (1 / sigma) in fp64,
 // rounds it once to fp32 and writes it to its u position in the wave's LDS
-// row; the row then goes out in 16-byte runs.  The pass is bound by HBM
-// bandwidth (6 bytes per bf16 element).
+// row; the row then goes out in 16-byte runs.  When H*D <= 2048 the passes
+// are unrolled: every load of the token is issued at once and the values stay
+// in registers for the second pass (larger rows loop and re-read them from
+// the caches).  The pass is bound by HBM bandwidth (6 bytes per bf16 element).
 #include <math.h>
 
 #include "common.h"
@@ -48,7 +50,8 @@ __device__ __forceinline__ void load_run(const void* x, size_t off, float* v) {
   }
 }
 
-template <bool XF32>
+// NIT > 0: H*D <= 512*NIT, the passes unrolled over registers; NIT = 0: any H*D
+template <bool XF32, int NIT>
 __global__ __launch_bounds__(256) void tasq_transform_kernel(TasqParams p) {
   extern __shared__ int tsm[];                // [H][D/2] inverse pair permutation, then one u row per wave
   const int s = blockIdx.y;
@@ -69,30 +72,9 @@ __global__ __launch_bounds__(256) void tasq_transform_kernel(TasqParams p) {
   const float* w = p.w + (size_t)step * HD;
   const size_t xoff = ((size_t)s * p.n_tok + j) * HD;
 
-  // sum of (w k)^2 over the token's H*D values, 8 consecutive values per lane and pass
-  double acc = 0.0;
-  for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-    float x[8], wv[8];
-    load_run<XF32>(p.xk, xoff + e0, x);
-    load_run<true>(w, e0, wv);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double y = (double)x[i] * (double)wv[i];
-      acc = fma(y, y, acc);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  const _Float16 s16 = (_Float16)(float)sqrt(acc / (double)HD);
-  if (lane == 0) p.sigma[(size_t)step * p.sigma_stride + p.slot_mapping[j]] = __builtin_bit_cast(uint16_t, s16);
-  const double inv = (float)s16 > 0.f ? 1.0 / (double)(float)s16 : 0.0;
-
   // u: key channel f of head h (f < D/2 or its partner f + D/2) goes to u
   // channel 2*inv[f] (or 2*inv[f] + 1) of that head, through the LDS row
-  for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-    float x[8], wv[8];
-    load_run<XF32>(p.xk, xoff + e0, x);
-    load_run<true>(w, e0, wv);
+  auto put_u = [&](int e0, const float* x, const float* wv, double inv) {
     const int h = e0 / D, f0 = e0 - h * D;
     const int side = f0 >= D2 ? 1 : 0, fq = f0 - side * D2;   // the 8 channels lie in one half
     float* dst = urow + h * D + side;
@@ -100,6 +82,88 @@ __global__ __launch_bounds__(256) void tasq_transform_kernel(TasqParams p) {
     for (int i = 0; i < 8; ++i) {
       const int pp = min(max(tinv[h * D2 + fq + i], 0), D2 - 1);
       dst[2 * pp] = (float)((double)x[i] * (double)wv[i] * inv);
+    }
+  };
+  // sigma in fp16 from the sum of (w k)^2 over the token's H*D values (it is
+  // written once per token); returns 1 / sigma, or 0 when sigma is 0
+  auto finish_sigma = [&](double acc) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    const _Float16 s16 = (_Float16)(float)sqrt(acc / (double)HD);
+    if (lane == 0) p.sigma[(size_t)step * p.sigma_stride + p.slot_mapping[j]] = __builtin_bit_cast(uint16_t, s16);
+    return (float)s16 > 0.f ? 1.0 / (double)(float)s16 : 0.0;
+  };
+
+  if constexpr (NIT > 0) {
+    // 8 consecutive values per lane and pass, every load issued before use;
+    // keys stay in their input words (bf16 pairs or fp32) until used
+    constexpr int XW = XF32 ? 8 : 4;
+    uint32_t xr[NIT][XW];
+    float wv[NIT][8];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int e0 = lane * 8 + it * 512;
+      if (e0 < HD) {
+        if constexpr (XF32) {
+          const uint4v a = *(const uint4v*)((const float*)p.xk + xoff + e0);
+          const uint4v b = *(const uint4v*)((const float*)p.xk + xoff + e0 + 4);
+          xr[it][0] = a.x; xr[it][1] = a.y; xr[it][2] = a.z; xr[it][3] = a.w;
+          xr[it][4] = b.x; xr[it][5] = b.y; xr[it][6] = b.z; xr[it][7] = b.w;
+        } else {
+          const uint4v a = *(const uint4v*)((const uint16_t*)p.xk + xoff + e0);
+          xr[it][0] = a.x; xr[it][1] = a.y; xr[it][2] = a.z; xr[it][3] = a.w;
+        }
+        load_run<true>(w, e0, wv[it]);
+      }
+    }
+    auto keys = [&](int it, float* x) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (XF32) x[i] = u2f(xr[it][i]);
+        else x[i] = (i & 1) ? bf16hi(xr[it][i >> 1]) : bf16lo(xr[it][i >> 1]);
+      }
+    };
+    double acc = 0.0;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (lane * 8 + it * 512 < HD) {
+        float x[8];
+        keys(it, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double y = (double)x[i] * (double)wv[it][i];
+          acc = fma(y, y, acc);
+        }
+      }
+    }
+    const double inv = finish_sigma(acc);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int e0 = lane * 8 + it * 512;
+      if (e0 < HD) {
+        float x[8];
+        keys(it, x);
+        put_u(e0, x, wv[it], inv);
+      }
+    }
+  } else {
+    double acc = 0.0;
+    for (int e0 = lane * 8; e0 < HD; e0 += 512) {
+      float x[8], wv[8];
+      load_run<XF32>(p.xk, xoff + e0, x);
+      load_run<true>(w, e0, wv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double y = (double)x[i] * (double)wv[i];
+        acc = fma(y, y, acc);
+      }
+    }
+    const double inv = finish_sigma(acc);
+    for (int e0 = lane * 8; e0 < HD; e0 += 512) {
+      float x[8], wv[8];
+      load_run<XF32>(p.xk, xoff + e0, x);
+      load_run<true>(w, e0, wv);
+      put_u(e0, x, wv, inv);
     }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's row is in LDS
@@ -119,8 +183,15 @@ hipError_t launch_tasq_transform(bool xf32, const TasqParams& p, int n_steps, hi
   const int wpb = (size_t)4 * HD * 4 + (size_t)HD * 2 <= 65536 ? 4 : 1;
   const dim3 grid((p.n_tok + wpb - 1) / wpb, n_steps);
   const size_t lds = (size_t)wpb * HD * 4 + (size_t)HD * 2;
-  if (xf32) hipLaunchKernelGGL(tasq_transform_kernel<true>, grid, dim3(64 * wpb), lds, s, p);
-  else hipLaunchKernelGGL(tasq_transform_kernel<false>, grid, dim3(64 * wpb), lds, s, p);
+#define LVQ_TQ(XF, NI) hipLaunchKernelGGL((tasq_transform_kernel<XF, NI>), grid, dim3(64 * wpb), lds, s, p)
+  if (HD <= 1024) {
+    if (xf32) LVQ_TQ(true, 2); else LVQ_TQ(false, 2);
+  } else if (HD <= 2048) {
+    if (xf32) LVQ_TQ(true, 4); else LVQ_TQ(false, 4);
+  } else {
+    if (xf32) LVQ_TQ(true, 0); else LVQ_TQ(false, 0);
+  }
+#undef LVQ_TQ
   return hipGetLastError();
 }
 
