@@ -12,8 +12,9 @@
 // from u as they would be from k.  A token whose fp16 sigma is 0 gets u = 0.
 //
 // MI355X mapping: one wave per (token, loop step), up to four tokens of one
-// step per workgroup.  The workgroup first inverts the block's pair
-// permutation into LDS.  The wave reads the token's H*D keys and weights in
+// step at a time per workgroup, and about four workgroups per CU that walk
+// their step's tokens.  The workgroup first inverts the block's pair
+// permutation into LDS, once.  The wave reads the token's H*D keys and weights in
 // 16-byte runs, sums the weighted squares in fp64 (the sum then matches an
 // exact evaluation except within fp64 rounding of an fp16 rounding midpoint)
 // and reduces across lanes with shuffles; every lane then holds sigma.  A
@@ -24,6 +25,8 @@
 // in registers for the second pass (larger rows loop and re-read them from
 // the caches).  The pass is bound by HBM bandwidth (6 bytes per bf16 element).
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -66,113 +69,116 @@ __global__ __launch_bounds__(256) void tasq_transform_kernel(TasqParams p) {
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = blockIdx.x * (blockDim.x >> 6) + wave;
-  if (j >= p.n_tok) return;                  // whole waves, after the only barrier
   float* urow = (float*)(tsm + p.H * D2) + (size_t)wave * HD;
   const float* w = p.w + (size_t)step * HD;
-  const size_t xoff = ((size_t)s * p.n_tok + j) * HD;
+  // the workgroup walks the step's tokens, one per wave at a time, so the
+  // inverse permutation is built once per workgroup
+  const int wpb = blockDim.x >> 6;
+  for (int j = blockIdx.x * wpb + wave; j < p.n_tok; j += gridDim.x * wpb) {
+    const size_t xoff = ((size_t)s * p.n_tok + j) * HD;
 
-  // u: key channel f of head h (f < D/2 or its partner f + D/2) goes to u
-  // channel 2*inv[f] (or 2*inv[f] + 1) of that head, through the LDS row
-  auto put_u = [&](int e0, const float* x, const float* wv, double inv) {
-    const int h = e0 / D, f0 = e0 - h * D;
-    const int side = f0 >= D2 ? 1 : 0, fq = f0 - side * D2;   // the 8 channels lie in one half
-    float* dst = urow + h * D + side;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pp = min(max(tinv[h * D2 + fq + i], 0), D2 - 1);
-      dst[2 * pp] = (float)((double)x[i] * (double)wv[i] * inv);
-    }
-  };
-  // sigma in fp16 from the sum of (w k)^2 over the token's H*D values (it is
-  // written once per token); returns 1 / sigma, or 0 when sigma is 0
-  auto finish_sigma = [&](double acc) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    const _Float16 s16 = (_Float16)(float)sqrt(acc / (double)HD);
-    if (lane == 0) p.sigma[(size_t)step * p.sigma_stride + p.slot_mapping[j]] = __builtin_bit_cast(uint16_t, s16);
-    return (float)s16 > 0.f ? 1.0 / (double)(float)s16 : 0.0;
-  };
-
-  if constexpr (NIT > 0) {
-    // 8 consecutive values per lane and pass, every load issued before use;
-    // keys stay in their input words (bf16 pairs or fp32) until used
-    constexpr int XW = XF32 ? 8 : 4;
-    uint32_t xr[NIT][XW];
-    float wv[NIT][8];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int e0 = lane * 8 + it * 512;
-      if (e0 < HD) {
-        if constexpr (XF32) {
-          const uint4v a = *(const uint4v*)((const float*)p.xk + xoff + e0);
-          const uint4v b = *(const uint4v*)((const float*)p.xk + xoff + e0 + 4);
-          xr[it][0] = a.x; xr[it][1] = a.y; xr[it][2] = a.z; xr[it][3] = a.w;
-          xr[it][4] = b.x; xr[it][5] = b.y; xr[it][6] = b.z; xr[it][7] = b.w;
-        } else {
-          const uint4v a = *(const uint4v*)((const uint16_t*)p.xk + xoff + e0);
-          xr[it][0] = a.x; xr[it][1] = a.y; xr[it][2] = a.z; xr[it][3] = a.w;
-        }
-        load_run<true>(w, e0, wv[it]);
-      }
-    }
-    auto keys = [&](int it, float* x) {
-#pragma unroll
+    // u: key channel f of head h (f < D/2 or its partner f + D/2) goes to u
+    // channel 2*inv[f] (or 2*inv[f] + 1) of that head, through the LDS row
+    auto put_u = [&](int e0, const float* x, const float* wv, double inv) {
+      const int h = e0 / D, f0 = e0 - h * D;
+      const int side = f0 >= D2 ? 1 : 0, fq = f0 - side * D2;   // the 8 channels lie in one half
+      float* dst = urow + h * D + side;
+  #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (XF32) x[i] = u2f(xr[it][i]);
-        else x[i] = (i & 1) ? bf16hi(xr[it][i >> 1]) : bf16lo(xr[it][i >> 1]);
+        const int pp = min(max(tinv[h * D2 + fq + i], 0), D2 - 1);
+        dst[2 * pp] = (float)((double)x[i] * (double)wv[i] * inv);
       }
     };
-    double acc = 0.0;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (lane * 8 + it * 512 < HD) {
-        float x[8];
-        keys(it, x);
-#pragma unroll
+    // sigma in fp16 from the sum of (w k)^2 over the token's H*D values (it is
+    // written once per token); returns 1 / sigma, or 0 when sigma is 0
+    auto finish_sigma = [&](double acc) {
+  #pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+      const _Float16 s16 = (_Float16)(float)sqrt(acc / (double)HD);
+      if (lane == 0) p.sigma[(size_t)step * p.sigma_stride + p.slot_mapping[j]] = __builtin_bit_cast(uint16_t, s16);
+      return (float)s16 > 0.f ? 1.0 / (double)(float)s16 : 0.0;
+    };
+
+    if constexpr (NIT > 0) {
+      // 8 consecutive values per lane and pass, every load issued before use;
+      // keys stay in their input words (bf16 pairs or fp32) until used
+      constexpr int XW = XF32 ? 8 : 4;
+      uint32_t xr[NIT][XW];
+      float wv[NIT][8];
+  #pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int e0 = lane * 8 + it * 512;
+        if (e0 < HD) {
+          if constexpr (XF32) {
+            const uint4v a = *(const uint4v*)((const float*)p.xk + xoff + e0);
+            const uint4v b = *(const uint4v*)((const float*)p.xk + xoff + e0 + 4);
+            xr[it][0] = a.x; xr[it][1] = a.y; xr[it][2] = a.z; xr[it][3] = a.w;
+            xr[it][4] = b.x; xr[it][5] = b.y; xr[it][6] = b.z; xr[it][7] = b.w;
+          } else {
+            const uint4v a = *(const uint4v*)((const uint16_t*)p.xk + xoff + e0);
+            xr[it][0] = a.x; xr[it][1] = a.y; xr[it][2] = a.z; xr[it][3] = a.w;
+          }
+          load_run<true>(w, e0, wv[it]);
+        }
+      }
+      auto keys = [&](int it, float* x) {
+  #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const double y = (double)x[i] * (double)wv[it][i];
+          if constexpr (XF32) x[i] = u2f(xr[it][i]);
+          else x[i] = (i & 1) ? bf16hi(xr[it][i >> 1]) : bf16lo(xr[it][i >> 1]);
+        }
+      };
+      double acc = 0.0;
+  #pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (lane * 8 + it * 512 < HD) {
+          float x[8];
+          keys(it, x);
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const double y = (double)x[i] * (double)wv[it][i];
+            acc = fma(y, y, acc);
+          }
+        }
+      }
+      const double inv = finish_sigma(acc);
+  #pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int e0 = lane * 8 + it * 512;
+        if (e0 < HD) {
+          float x[8];
+          keys(it, x);
+          put_u(e0, x, wv[it], inv);
+        }
+      }
+    } else {
+      double acc = 0.0;
+      for (int e0 = lane * 8; e0 < HD; e0 += 512) {
+        float x[8], wv[8];
+        load_run<XF32>(p.xk, xoff + e0, x);
+        load_run<true>(w, e0, wv);
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double y = (double)x[i] * (double)wv[i];
           acc = fma(y, y, acc);
         }
       }
-    }
-    const double inv = finish_sigma(acc);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int e0 = lane * 8 + it * 512;
-      if (e0 < HD) {
-        float x[8];
-        keys(it, x);
-        put_u(e0, x, wv[it], inv);
+      const double inv = finish_sigma(acc);
+      for (int e0 = lane * 8; e0 < HD; e0 += 512) {
+        float x[8], wv[8];
+        load_run<XF32>(p.xk, xoff + e0, x);
+        load_run<true>(w, e0, wv);
+        put_u(e0, x, wv, inv);
       }
     }
-  } else {
-    double acc = 0.0;
+    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's row is in LDS
+    __asm__ __volatile__("" ::: "memory");
     for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-      float x[8], wv[8];
-      load_run<XF32>(p.xk, xoff + e0, x);
-      load_run<true>(w, e0, wv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double y = (double)x[i] * (double)wv[i];
-        acc = fma(y, y, acc);
-      }
+      const float4v a = *(const float4v*)(urow + e0), b = *(const float4v*)(urow + e0 + 4);
+      float* out = p.u + xoff + e0;
+      *(float4v*)out = a;
+      *(float4v*)(out + 4) = b;
     }
-    const double inv = finish_sigma(acc);
-    for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-      float x[8], wv[8];
-      load_run<XF32>(p.xk, xoff + e0, x);
-      load_run<true>(w, e0, wv);
-      put_u(e0, x, wv, inv);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's row is in LDS
-  __asm__ __volatile__("" ::: "memory");
-  for (int e0 = lane * 8; e0 < HD; e0 += 512) {
-    const float4v a = *(const float4v*)(urow + e0), b = *(const float4v*)(urow + e0 + 4);
-    float* out = p.u + xoff + e0;
-    *(float4v*)out = a;
-    *(float4v*)(out + 4) = b;
   }
 }
 
@@ -181,7 +187,10 @@ hipError_t launch_tasq_transform(bool xf32, const TasqParams& p, int n_steps, hi
   const int HD = p.H * p.D;
   // four tokens per workgroup while their rows fit next to the permutation in 64 KiB
   const int wpb = (size_t)4 * HD * 4 + (size_t)HD * 2 <= 65536 ? 4 : 1;
-  const dim3 grid((p.n_tok + wpb - 1) / wpb, n_steps);
+  // about four resident workgroups per CU over all steps; each walks its
+  // step's tokens
+  const int per_step = std::max(1, 1024 / n_steps);
+  const dim3 grid(std::min((p.n_tok + wpb - 1) / wpb, per_step), n_steps);
   const size_t lds = (size_t)wpb * HD * 4 + (size_t)HD * 2;
 #define LVQ_TQ(XF, NI) hipLaunchKernelGGL((tasq_transform_kernel<XF, NI>), grid, dim3(64 * wpb), lds, s, p)
   if (HD <= 1024) {

@@ -45,6 +45,9 @@ def _random_sigma(cfg, n_slots, seed):
     ("gqa_ragged", dict(H_kv=2, H_q=8), 200),        # c = 8
     ("tiny", dict(bits=8), 256),                     # D = 64, c = 2, fp32 input
     ("deeploop", dict(H_kv=2, H_q=2), 64),           # eight blocks
+    # 32 loop steps share the transform's workgroups, so each walks several
+    # groups of four tokens (the last one partial)
+    ("deeploop", dict(H_kv=2, H_q=2), 300),
 ])
 def test_tasq_encode(name, over, n_tok):
     cfg = synth.config_by_name(name).replace(n_calib=400, **over)
