@@ -150,7 +150,9 @@ size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D);
  *   cb, hsq       codebooks and 0.5*||e||^2 of blocks first_block ..
  *                 first_block+n_blocks-1, layouts as above (hsq from
  *                 loopvq_build_codebook_slices).
- *   slot_mapping  [n_tok] int32 physical slot page*P + offset of each token.
+ *   slot_mapping  [n_tok] int32 physical slot page*P + offset of each token,
+ *                 in [0, num_pages*P) (device data, not checked: a slot
+ *                 outside the cache writes outside it).
  *   index_cache   cache of block first_block; block beta's cache starts at
  *                 index_cache + (beta - first_block)*block_stride_bytes.
  * Distances are evaluated as ||z||^2 - 2 z.e + ||e||^2 with fp16 inputs and
@@ -208,7 +210,9 @@ size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
  *   index_cache   the cache of block (t-1)/Tc.
  *   slices        [T][H_kv][2][K][c] fp16 from loopvq_build_codebook_slices.
  *   rope_table    device copy of loopvq_rope_table(max_pos, D, base).
- *   block_table   [B][max_pages] int32 physical page of each logical page.
+ *   block_table   [B][max_pages] int32 physical page of each logical page,
+ *                 in [0, num_pages) for every logical page a request's
+ *                 seq_len covers (device data, not checked).
  *   seq_lens      [B] int32 cached tokens per request, 0 <= seq_lens[b] <=
  *                 max_seq_len, and max_seq_len <= max_pos, and
  *                 max_seq_len <= max_pages*P.  Token j of a request sits at
