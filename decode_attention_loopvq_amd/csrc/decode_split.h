@@ -232,8 +232,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      (q_h = q_{f + D/2}; pair 0 and pair 1 of the duo), so that with the
   //      key column (k0_f, k0_h, k1_f, k1_h) of a position the MFMA yields
   //      X0, Y0, X1, Y1 of that position.
+  //      fp32 queries (QF32): the same row of each pair, each coefficient as an
+  //      fp16 high and low part along the reduction index, A row =
+  //      (x_f hi, x_h hi, x_f lo, x_h lo) against the key column
+  //      (k_f, k_h, k_f, k_h) of one stream, so one product covers both pairs
+  //      when they share keys and two (one per stream) when they do not.
   half4v AK[F];
-  half4v AKl[(QF32 && !TQ) ? F : 1];
   // TaSQ: u pair of the lane's i-th frequency slot: the pairs of its quarter's
   // lo groups, then those of its hi groups
   auto tq_upair = [&](int i) { return i < F / 2 ? la * (F / 2) + i : D / 4 + la * (F / 2) + (i - F / 2); };
@@ -281,10 +285,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const float x0 = (lb & 1) ? c : a, x1 = (lb & 1) ? -a : c;
       const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
       const _Float16 z = (_Float16)0.f;
-      AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
-      if constexpr (QF32 && !TQ) {
-        const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-        AKl[i] = s ? (half4v){z, z, l0, l1} : (half4v){l0, l1, z, z};
+      if constexpr (QF32) {
+        AK[i] = (half4v){h0, h1, (_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
+      } else {
+        AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
       }
     }
   }
@@ -468,9 +472,18 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const uint32_t w0 = perm(khi[0][r].d[e >> 1], klo[0][r].d[e >> 1], sel);   // (k0_f, k0_h)
         const uint32_t w1 = SHARE ? w0 : perm(khi[NS - 1][r].d[e >> 1], klo[NS - 1][r].d[e >> 1], sel);
-        const half4v Bk = __builtin_bit_cast(half4v, (uint2v){w0, w1});
-        xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], Bk, zero, 0, 0, 0);
-        if constexpr (QF32) xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AKl[i], Bk, xy, 0, 0, 0);
+        if constexpr (QF32) {
+          // rows 0-1 (pair 0) against stream 0's key, rows 2-3 against stream 1's
+          xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w0, w0}), zero, 0, 0, 0);
+          if constexpr (!SHARE) {
+            const float4v xy1 =
+                __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w1, w1}), zero, 0, 0, 0);
+            xy.z = xy1.z;
+            xy.w = xy1.w;
+          }
+        } else {
+          xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w0, w1}), zero, 0, 0, 0);
+        }
       }
       const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
       const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     // interleave: each MFMA is followed by VALU work (the next perms and this
     // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
-    constexpr int KMF = TQ ? (SHARE ? 1 : 2) : (QF32 ? 2 : 1);
+    constexpr int KMF = (TQ || QF32) ? (SHARE ? 1 : 2) : 1;
     constexpr int KVALU = TQ ? 4 : 6;
 #pragma unroll
     for (int i = 0; i < F; ++i) {

@@ -233,6 +233,28 @@ def test_page_sizes(page_size):
     assert compare(cfg, o, lse, ref, lens)[1] <= 1.0
 
 
+@pytest.mark.parametrize("over,lens", [
+    # fp32 queries and outputs on each K-side form: the duo's pairs share keys
+    # (GQA), or not, with whole-step pages and with 8-token pages
+    (dict(H_kv=4, H_q=8), [700, 1, 0, 300]),
+    (dict(H_kv=4, H_q=8, page_size=8), [600, 37]),
+    (dict(H_kv=4, H_q=4, page_size=8), [600, 37]),
+])
+def test_fp32_io_paths(over, lens):
+    cfg = synth.config_by_name("layer1p4b").replace(io_dtype="f32", **over)
+    lens = np.array(lens)
+    bt, npg, caches = _random_cache_case(cfg, lens, 31)
+    cb = synth.make_codebooks(cfg.replace(n_calib=300))
+    layer = GpuLayer(cfg, cb, int(lens.max()))
+    q = synth.make_queries(cfg, len(lens), t=4)
+    _note(f"fp32 io decode {over} lens={list(lens)}")
+    o, lse = layer.decode(4, q, caches[0], bt, lens)
+    ref = ref_decode(cfg, 4, q, caches[0], bt, lens, cb)
+    err, ratio = compare(cfg, o, lse, ref, lens)
+    _note(f"fp32 io decode {over}: max err {err:.2e}")
+    assert err < 1e-4
+
+
 def test_per_step_coding_runs_on_the_same_kernels():
     # Tc = 1: every loop step has its own codebook and its own cache block
     cfg = synth.config_by_name("layer1p4b").replace(Tc=1, c=8, H_kv=2, H_q=2,
