@@ -16,6 +16,8 @@ codebook per channel group ("per_group"), TaSQ-coded keys on the same batch
 and the TaSQ transform + coding of the prefill ("tasq"), the encoder on the
 prefill of the 1.4B-layer workload (8 x 4096 tokens, "encode"), and one
 k-means Lloyd iteration over that prefill's coupled vectors ("kmeans").
+The fp64 oracle is timed on the host beside it: on one core over a bounded
+sample, and on all cores (one request per worker process) over the batch.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -457,6 +459,57 @@ def cpu_baseline(np, synth, dec, budget_s: float = 12.0):
             "cpu_model": model, "host_cpus": nproc}
 
 
+def _oracle_worker_start(_):
+    """Warm a worker of the all-cores baseline (imports the oracle, one BLAS thread)."""
+    import oracle  # noqa: F401  (test infrastructure: used only for this reference timing)
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+    return os.getpid()
+
+
+def _oracle_request(task):
+    """One request of the decode workload through the oracle, on the request's own pages."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    q, pages, n, cb, Tc, c, bits, base = task
+    with threadpool_limits(limits=1):
+        oracle.decode_attention(q, pages, np.arange(pages.shape[0], dtype=np.int32), n, cb, 1, Tc, c, bits, base)
+    return n
+
+
+def cpu_baseline_all_cores(np, dec, max_workers: int = 16):
+    """The same oracle over every request of the batch, one request per worker process
+    (spawned, one BLAS thread each) on the host's cores; each task carries only its
+    request's pages.  Worker start-up is excluded from the timing."""
+    import concurrent.futures
+    import multiprocessing
+    cfg = dec["cfg"]
+    cache = dec["cache"][0].cpu().numpy()
+    cb = dec["cb"].cpu().numpy()[0]
+    q = dec["qs"][0].float().cpu().numpy()
+    lens, bt = dec["lens"], dec["bt_np"]
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    workers = max(1, min(max_workers, avail, len(lens)))
+    tasks = []
+    for b in range(len(lens)):
+        n = int(lens[b])
+        npg = (n + cfg.page_size - 1) // cfg.page_size
+        tasks.append((q[b], np.ascontiguousarray(cache[bt[b][:npg]]), n, cb, cfg.Tc, cfg.c, cfg.bits, cfg.base))
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        list(ex.map(_oracle_worker_start, range(workers)))
+        t0 = time.perf_counter()
+        tokens = sum(ex.map(_oracle_request, tasks))
+        el = time.perf_counter() - t0
+    return {"value": tokens / el, "unit": "cached tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {len(lens)} requests of the same 32K-context batch (all 16 KV heads, loop "
+                      f"step 1), one request per worker process, {el:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,7 +548,10 @@ def main():
     tqr = bench_tasq(args, torch, np, synth, lv, dec)
     enc = None if args.skip_encode else bench_encode(args, torch, np, synth, lv)
     kms = None if args.skip_encode else bench_kmeans(args, torch, np, synth, lv)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(np, synth, dec)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, synth, dec)
+        cpu["all_cores"] = cpu_baseline_all_cores(np, dec)
     cfg = dec["cfg"]
     line = {
         "metric": METRIC,
