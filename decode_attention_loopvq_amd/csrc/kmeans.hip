@@ -12,11 +12,15 @@
 //
 // MI355X mapping: a workgroup takes a range of tokens of one stream; each
 // thread takes one coupled vector at a time (its code from the index row, its
-// G values as Tc runs of c channels), adds it into per-entry fp64 sums in LDS
-// (ds_add_f64) and counts the entry, and the workgroup then adds its LDS sums
-// into the stream's fp64 sums in global memory.  fp64 sums of bf16 or fp16
-// values are exact, so the result does not depend on the order of the adds.
-// A second kernel divides and rounds.
+// G values as Tc runs of c channels, one vector load per run), adds it into
+// per-entry fp64 sums in LDS (ds_add_f64), counts the entry and sums ||z||^2,
+// and the workgroup then adds its LDS sums into the stream's fp64 sums in
+// global memory.  fp64 sums of bf16 or fp16 values are exact, so the result
+// does not depend on the order of the adds.  A second kernel, one workgroup
+// per stream, divides and rounds, and forms the error from the same sums:
+// sum_v ||z_v - e_code(v)||^2 = sum_v ||z_v||^2 - 2 sum_r e_r . S_r
+// + sum_r n_r ||e_r||^2 with S_r and n_r the sum and count of entry r, so the
+// first kernel never reads the codebook.
 #include <math.h>
 
 #include <algorithm>
@@ -30,16 +34,52 @@ __global__ void kmeans_zero_kernel(double* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0.0;
 }
 
-template <int G, bool XF32>
+// the C channels of one loop step of a coupled vector, as floats
+template <int C, bool XF32>
+__device__ __forceinline__ void load_channels(const void* x, size_t off, float* z) {
+  if constexpr (XF32) {
+    const float* s = (const float*)x + off;
+    if constexpr (C == 2) {
+      const float2v a = *(const float2v*)s;
+      z[0] = a.x; z[1] = a.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < C / 4; ++j) {
+        const float4v a = *(const float4v*)(s + 4 * j);
+        z[4 * j] = a.x; z[4 * j + 1] = a.y; z[4 * j + 2] = a.z; z[4 * j + 3] = a.w;
+      }
+    }
+  } else {
+    const uint16_t* s = (const uint16_t*)x + off;
+    uint32_t w[C / 2];
+    if constexpr (C == 2) {
+      w[0] = *(const uint32_t*)s;
+    } else if constexpr (C == 4) {
+      const uint2v a = *(const uint2v*)s;
+      w[0] = a.x; w[1] = a.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < C / 8; ++j) {
+        const uint4v a = *(const uint4v*)(s + 8 * j);
+        w[4 * j] = a.x; w[4 * j + 1] = a.y; w[4 * j + 2] = a.z; w[4 * j + 3] = a.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) z[i] = (i & 1) ? bf16hi(w[i >> 1]) : bf16lo(w[i >> 1]);
+  }
+}
+
+template <int G, int C, bool XF32>
 __global__ __launch_bounds__(256) void kmeans_accum_kernel(KmeansParams p) {
   // per-entry sums with rows of G + 1 doubles (the odd stride spreads the random
-  // entries of a wave over the LDS banks), then [K] counts and [2] error sums
+  // entries of a wave over the LDS banks), then [K] counts and [2] (unused, ||z||^2)
   constexpr int GS = G + 1;
+  constexpr int TC = G / C;
   __shared__ double kms[256 * GS + 256 + 2];
-  const int K = p.K, H = p.H_kv, C = p.c, Tc = p.Tc, D = p.D;
+  const int K = p.K, H = p.H_kv, D = p.D;
   double* s_sum = kms;
   double* s_cnt = kms + (size_t)K * GS;
-  double* s_err = s_cnt + K;
+  double* s_nrm = s_cnt + K + 1;
   for (int i = threadIdx.x; i < K * GS + K + 2; i += blockDim.x) kms[i] = 0.0;
   __syncthreads();
 
@@ -49,10 +89,9 @@ __global__ __launch_bounds__(256) void kmeans_accum_kernel(KmeansParams p) {
   const int P = 1 << p.log2P;
   const int R = n * p.bits / 8;
   const void* x = kv ? p.xv : p.xk;
-  const uint16_t* cb = p.cb + ((size_t)(beta * H + h) * 2 + kv) * K * G;
   const uint8_t* cache = p.cache + (int64_t)beta * p.block_stride;
   const int t0 = blockIdx.x * p.tok_per_wg, t1 = min(t0 + p.tok_per_wg, p.n_tok);
-  double err = 0.0, nrm = 0.0;
+  double nrm = 0.0;
   for (int v = t0 * n + threadIdx.x; v < t1 * n; v += blockDim.x) {
     const int tok = v / n, g = v - tok * n;
     const int slot = p.slot_mapping[tok];
@@ -61,31 +100,23 @@ __global__ __launch_bounds__(256) void kmeans_accum_kernel(KmeansParams p) {
     int code;
     if (p.bits == 8) code = row[sl];
     else code = (row[sl >> 1] >> ((sl & 1) * 4)) & 15;
-    const uint16_t* e = cb + (size_t)code * G;
     double* acc = s_sum + (size_t)code * GS;
-    for (int m = 0; m < Tc; ++m) {
-      const size_t off = (((size_t)(beta * Tc + m) * p.n_tok + tok) * H + h) * D + (size_t)g * C;
+#pragma unroll
+    for (int m = 0; m < TC; ++m) {
+      float z[C];
+      load_channels<C, XF32>(x, (((size_t)(beta * TC + m) * p.n_tok + tok) * H + h) * D + (size_t)g * C, z);
+#pragma unroll
       for (int i = 0; i < C; ++i) {
-        double z;
-        if constexpr (XF32) z = (double)((const float*)x)[off + i];
-        else z = (double)u2f((uint32_t)((const uint16_t*)x)[off + i] << 16);
-        const double d = z - (double)__builtin_bit_cast(_Float16, e[i * Tc + m]);
-        err = fma(d, d, err);
-        nrm = fma(z, z, nrm);
-        atomicAdd(acc + i * Tc + m, z);
+        const double zd = (double)z[i];
+        nrm = fma(zd, zd, nrm);
+        atomicAdd(acc + i * TC + m, zd);
       }
     }
     atomicAdd(s_cnt + code, 1.0);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    err += __shfl_xor(err, o);
-    nrm += __shfl_xor(nrm, o);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    atomicAdd(s_err, err);
-    atomicAdd(s_err + 1, nrm);
-  }
+  for (int o = 32; o > 0; o >>= 1) nrm += __shfl_xor(nrm, o);
+  if ((threadIdx.x & 63) == 0) atomicAdd(s_nrm, nrm);
   __syncthreads();
   double* gsum = p.gsum + (size_t)y * (K * G + K + 2);
   for (int i = threadIdx.x; i < K * G + K + 2; i += blockDim.x) {
@@ -94,24 +125,32 @@ __global__ __launch_bounds__(256) void kmeans_accum_kernel(KmeansParams p) {
   }
 }
 
-// entry e of stream y: mean of its vectors rounded to fp16, or unchanged
-__global__ void kmeans_finalize_kernel(KmeansParams p, int G, int n_streams) {
+// one workgroup per stream y: entry e becomes the mean of its vectors rounded to
+// fp16, or stays unchanged; the stream's error and ||z||^2 sums are written
+__global__ __launch_bounds__(256) void kmeans_finalize_kernel(KmeansParams p, int G) {
+  __shared__ double red[4];
   const int K = p.K, H = p.H_kv;
-  const size_t total = (size_t)n_streams * K * G;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int y = (int)(i / ((size_t)K * G));
-    const int r = (int)(i - (size_t)y * K * G);
-    const int e = r / G;
-    const int h = y % H, kv = (y / H) & 1, beta = y / (2 * H);
-    const size_t ci = (((size_t)(beta * H + h) * 2 + kv) * K) * G + r;
-    const double* gs = p.gsum + (size_t)y * (K * G + K + 2);
-    const double cnt = gs[(size_t)K * G + e];
-    p.cb_out[ci] = cnt > 0.0 ? __builtin_bit_cast(uint16_t, (_Float16)(gs[r] / cnt)) : p.cb[ci];
-    if (r == 0 && p.err != nullptr) {
-      const size_t eo = (((size_t)(beta * H + h) * 2 + kv)) * 2;
-      p.err[eo] = gs[(size_t)K * G + K];
-      p.err[eo + 1] = gs[(size_t)K * G + K + 1];
-    }
+  const int y = blockIdx.x;
+  const int h = y % H, kv = (y / H) & 1, beta = y / (2 * H);
+  const size_t c0 = (((size_t)(beta * H + h) * 2 + kv) * K) * G;
+  const double* gs = p.gsum + (size_t)y * (K * G + K + 2);
+  double part = 0.0;                        // sum_r n_r ||e_r||^2 - 2 e_r . S_r
+  for (int r = threadIdx.x; r < K * G; r += blockDim.x) {
+    const double cnt = gs[(size_t)K * G + r / G];
+    const uint16_t old = p.cb[c0 + r];
+    const double e = (double)__builtin_bit_cast(_Float16, old);
+    part = fma(e, fma(cnt, e, -2.0 * gs[r]), part);
+    p.cb_out[c0 + r] = cnt > 0.0 ? __builtin_bit_cast(uint16_t, (_Float16)(gs[r] / cnt)) : old;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  if (threadIdx.x == 0 && p.err != nullptr) {
+    const double nrm = gs[(size_t)K * G + K + 1];
+    const size_t eo = (((size_t)(beta * H + h) * 2 + kv)) * 2;
+    p.err[eo] = nrm + ((red[0] + red[1]) + (red[2] + red[3]));
+    p.err[eo + 1] = nrm;
   }
 }
 
@@ -124,17 +163,17 @@ hipError_t launch_kmeans_update(bool xf32, const KmeansParams& p, int n_blocks, 
                      p.gsum, nz);
   if (p.n_tok > 0) {
     const dim3 grid((p.n_tok + p.tok_per_wg - 1) / p.tok_per_wg, n_streams);
-#define LVQ_KM(g)                                                                                  \
-    if (G == g) {                                                                                  \
-      if (xf32) hipLaunchKernelGGL((kmeans_accum_kernel<g, true>), grid, dim3(256), 0, s, p);     \
-      else hipLaunchKernelGGL((kmeans_accum_kernel<g, false>), grid, dim3(256), 0, s, p);         \
+#define LVQ_KM(GG, CC)                                                                                  \
+    if (G == GG && p.c == CC) {                                                                         \
+      if (xf32) hipLaunchKernelGGL((kmeans_accum_kernel<GG, CC, true>), grid, dim3(256), 0, s, p);     \
+      else hipLaunchKernelGGL((kmeans_accum_kernel<GG, CC, false>), grid, dim3(256), 0, s, p);         \
     }
-    LVQ_KM(8) LVQ_KM(16) LVQ_KM(32)
+    LVQ_KM(8, 2) LVQ_KM(8, 4) LVQ_KM(8, 8)
+    LVQ_KM(16, 2) LVQ_KM(16, 4) LVQ_KM(16, 8) LVQ_KM(16, 16)
+    LVQ_KM(32, 2) LVQ_KM(32, 4) LVQ_KM(32, 8)
 #undef LVQ_KM
   }
-  const size_t tot = (size_t)n_streams * p.K * G;
-  hipLaunchKernelGGL(kmeans_finalize_kernel, dim3((unsigned)std::min<size_t>((tot + 255) / 256, 4096)), dim3(256), 0,
-                     s, p, G, n_streams);
+  hipLaunchKernelGGL(kmeans_finalize_kernel, dim3(n_streams), dim3(256), 0, s, p, G);
   return hipGetLastError();
 }
 
