@@ -74,8 +74,14 @@ DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   // about 2048 waves (8 per CU) over the whole call
   long long Lc = (work + 2047) / 2048;
   Lc = (Lc + step2 - 1) / step2 * step2;
-  // shared rows keep each chunk's page ids in a 128-entry list per stream
-  if (pl.shared_rope) Lc = std::min(Lc, (126LL * d->page_size) / step2 * step2);
+  // shared rows keep each chunk's page ids in a DECODE_PAGE_LIST-entry list
+  // per stream.  Chunks start at multiples of Lc, a multiple of step2: when
+  // the page size divides step2 they start on a page boundary and span at most
+  // Lc / P pages; otherwise at most Lc / P + 1
+  if (pl.shared_rope) {
+    const long long pages = step2 % d->page_size == 0 ? DECODE_PAGE_LIST : DECODE_PAGE_LIST - 1;
+    Lc = std::min(Lc, (pages * d->page_size) / step2 * step2);
+  }
   Lc = std::max(Lc, step2);
   Lc = std::min(Lc, (len + step2 - 1) / step2 * step2);
   pl.Lc = (int)Lc;

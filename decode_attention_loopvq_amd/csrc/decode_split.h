@@ -135,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // one codebook per group (PG), the N*KENT entries of each of K and V packed
   constexpr int LDS_SLICES = PG ? 2 * N * KENT * EB : 2 * KENT * 256;
   constexpr int LDS_RING = ST ? 2 * TSTEP : 0;
-  constexpr int PGMAX = 128;          // page-list entries per stream and wave (shared rows)
+  constexpr int PGMAX = DECODE_PAGE_LIST;   // page-list entries per stream and wave (shared rows)
   constexpr int LDS_PAGES = ST ? WAVES * 2 * PGMAX * 4 : 0;
   constexpr int LDS_MERGE = WAVES * 64 * SW * 4;
   constexpr int LDS_BYTES = LDS_SLICES + LDS_RING + LDS_PAGES > LDS_MERGE ? LDS_SLICES + LDS_RING + LDS_PAGES

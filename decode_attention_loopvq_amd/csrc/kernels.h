@@ -7,6 +7,10 @@
 
 namespace loopvq {
 
+// entries of the per-wave page lists of the workgroup-shared RoPE path (per
+// stream): a chunk of the split plan must span at most this many pages
+constexpr int DECODE_PAGE_LIST = 128;
+
 struct DecodeParams {
   const void* q;              // [B][H_q][D] bf16 or fp32
   const uint8_t* cache;       // [num_pages][H_kv][2][P][R]

@@ -136,6 +136,22 @@ def test_full_size_decode_sampled(name, t_list, requests, heads):
         assert ratio <= 1.0
 
 
+def test_full_size_decode_16_token_pages():
+    # 16-token pages at the 32K batch: the shared-rows split plan fills each
+    # chunk's page list exactly (2048-position chunks of 128 pages)
+    cfg = synth.config_by_name("longctx32k").replace(page_size=16)
+    lens = synth.make_seq_lens(cfg)
+    bt, npg, caches = _random_cache_case(cfg, lens, 78)
+    cb = synth.make_codebooks(cfg)
+    layer = GpuLayer(cfg, cb, int(lens.max()))
+    q = synth.make_queries(cfg, len(lens), t=2)
+    o, lse = layer.decode(2, q, to_dev(caches[0]), bt, lens)
+    ref = ref_decode(cfg, 2, q, caches[0], bt, lens, cb, requests=(0, 15), heads=(0, 15))
+    err, ratio = compare(cfg, o, lse, ref, lens)
+    _note(f"longctx32k, 16-token pages: max err {err:.2e} (bound ratio {ratio:.2f})")
+    assert ratio <= 1.0
+
+
 def test_gqa_ragged_decode():
     cfg = synth.config_by_name("gqa_ragged")
     # small ragged batch, every pair checked
