@@ -310,10 +310,15 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // a page's offset is one 32 x 32 -> 64-bit product of unsigned values
   const uint32_t page_stride = (uint32_t)p.H_kv * 2u * kv_stride;
   const uint8_t* head_base = p.cache + (size_t)h * 2 * kv_stride;
-  // byte offsets of the lane's K and V row quarters from the first row of
-  // its group: the whole step inside one page (SP), or the row's own 4
-  // positions (pages of 8 positions)
-  const uint32_t kro = (uint32_t)(((SP ? 4 * row : 0) + lb) * R + la * LB);
+  // pages of 8 positions: wave-uniform page ids (two per stream and step, see
+  // page_at) except with TaSQ keys, whose per-wave-row path keeps per-lane page
+  // ids (uniform ones cost it more registers than it has)
+  constexpr bool P8U = !SP && !TQ;
+  // byte offsets of the lane's K and V row quarters from the first row of the
+  // step (the whole step inside one page, SP), of the lane's page (P8U:
+  // positions 0-7 of a step in one page, 8-15 in the next), or of the lane's
+  // own 4-position row group
+  const uint32_t kro = (uint32_t)(((SP ? 4 * row : (P8U ? 4 * (row & 1) : 0)) + lb) * R + la * LB);
   const uint32_t vro = kv_stride + (uint32_t)(((SP ? 8 * rp : 0) + 2 * la) * R + lb * LB);   // +R: slot b
   const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
   int lim[2], last[2];
@@ -336,16 +341,24 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   const int vz = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
 
   // raw block-table entries of the step's pages (only trusted when the
-  // stream's length is positive): one per stream with whole-step pages (SP);
-  // else per lane, one per stream for the K row group and one for the V groups
-  constexpr int NPG = SP ? NS : NS + 1;
+  // stream's length is positive).  SP: one per stream, wave-uniform.  P8U: two
+  // per stream, wave-uniform, the page of the step's positions 0-7 and that
+  // of 8-15 (a step starts on a multiple of 16).  Else per lane, one per
+  // stream for the K row group and one for the V groups
+  constexpr int NPG = SP ? NS : (P8U ? 2 * NS : NS + 1);
   auto page_at = [&](int st, int* pg) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if constexpr (SP) pg[s] = btb[s][(min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) + vz];
-      else pg[s] = btb[s][min(max(p0 + st * NT + 4 * row, lo[s]), last[s]) >> p.log2P];
+      if constexpr (SP) {
+        pg[s] = btb[s][(min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) + vz];
+      } else if constexpr (P8U) {
+        pg[2 * s] = btb[s][(min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) + vz];
+        pg[2 * s + 1] = btb[s][(min(max(p0 + st * NT + 8, lo[s]), last[s]) >> p.log2P) + vz];
+      } else {
+        pg[s] = btb[s][min(max(p0 + st * NT + 4 * row, lo[s]), last[s]) >> p.log2P];
+      }
     }
-    if constexpr (!SP) pg[NS] = btb[sv][min(max(p0 + st * NT + 8 * rp, lo[sv]), last[sv]) >> p.log2P];
+    if constexpr (!SP && !P8U) pg[NS] = btb[sv][min(max(p0 + st * NT + 8 * rp, lo[sv]), last[sv]) >> p.log2P];
   };
   // K rows of both streams at the lane's K position, V rows of stream sv at
   // the lane's two V positions
@@ -367,6 +380,25 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       }
       vbase = (NS == 1 || sv == 0) ? base[0] : base[NS - 1];
       vslot = (NS == 1 || sv == 0) ? slot0[0] : slot0[NS - 1];
+    } else if constexpr (P8U) {
+      // page A holds the step's positions 0-7 (K rows of lane rows 0-1, V rows
+      // of rp = 0), page B positions 8-15; both start at row 0 of their page.
+      // Past the end of a stream both clamp to its last page (rows read there
+      // are in bounds and masked)
+      const uint8_t* vb[2];
+      size_t vs[2];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint32_t pga = has[s] ? (uint32_t)__builtin_amdgcn_readfirstlane(raw_page[2 * s]) : 0u;
+        const uint32_t pgb = has[s] ? (uint32_t)__builtin_amdgcn_readfirstlane(raw_page[2 * s + 1]) : 0u;
+        const uint8_t* ba = head_base + (uint64_t)pga * page_stride;
+        const uint8_t* bb = head_base + (uint64_t)pgb * page_stride;
+        RowLoad<LB>::load((row >= 2 ? bb : ba) + kro, kw[s]);
+        vb[s] = rp ? bb : ba;
+        vs[s] = (size_t)(rp ? pgb : pga) * P;
+      }
+      vbase = (NS == 1 || sv == 0) ? vb[0] : vb[NS - 1];
+      vslot = (NS == 1 || sv == 0) ? vs[0] : vs[NS - 1];
     } else {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
