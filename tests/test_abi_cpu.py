@@ -261,6 +261,21 @@ def test_workspace_bytes_monotone(L):
     assert L.loopvq_decode_workspace_bytes(d, -1, 10) == 0
 
 
+def test_split_plan_chunks_with_16_token_pages(L):
+    # 16 requests x 32768 tokens, 16 heads: 2048-position chunks (16 per request)
+    # whether pages hold 64 or 16 positions; with 16-position pages each chunk's
+    # page list (128 entries per stream) is then exactly full.  The workspace
+    # holds one (o, lse) partial per chunk, D + 1 floats per (head, pair, chunk)
+    for P in (64, 16):
+        d = _dims(L, page_size=P)
+        assert L.loopvq_decode_workspace_bytes(d, 16, 32768) == \
+            L.loopvq_decode_workspace_bytes(_dims(L), 16, 32768)
+    n_part = 16 * 16 * 16
+    parts = ((n_part * 128 * 4 + 255) // 256 * 256) + ((n_part * 4 + 255) // 256 * 256)
+    window = ((16 * 16 * 128 * 4 + 255) // 256 * 256) + ((16 * 16 * 4 + 255) // 256 * 256)
+    assert L.loopvq_decode_workspace_bytes(_dims(L, page_size=16), 16, 32768) == parts + window
+
+
 @pytest.mark.parametrize("D,max_pos", [(64, 40001), (128, 40000)])
 def test_rope_table_matches_oracle(L, D, max_pos):
     t = L.loopvq_rope_table(max_pos, D).numpy()
