@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void kmeans_accum_kernel(KmeansParams p) {
 
 // one workgroup per stream y: entry e becomes the mean of its vectors rounded to
 // fp16, or stays unchanged; the stream's error and ||z||^2 sums are written
-__global__ __launch_bounds__(256) void kmeans_finalize_kernel(KmeansParams p, int G) {
-  __shared__ double red[4];
+__global__ __launch_bounds__(1024) void kmeans_finalize_kernel(KmeansParams p, int G) {
+  __shared__ double red[16];
   const int K = p.K, H = p.H_kv;
   const int y = blockIdx.x;
   const int h = y % H, kv = (y / H) & 1, beta = y / (2 * H);
@@ -147,9 +147,11 @@ __global__ __launch_bounds__(256) void kmeans_finalize_kernel(KmeansParams p, in
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
   __syncthreads();
   if (threadIdx.x == 0 && p.err != nullptr) {
+    double tot = 0.0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
     const double nrm = gs[(size_t)K * G + K + 1];
     const size_t eo = (((size_t)(beta * H + h) * 2 + kv)) * 2;
-    p.err[eo] = nrm + ((red[0] + red[1]) + (red[2] + red[3]));
+    p.err[eo] = nrm + tot;
     p.err[eo + 1] = nrm;
   }
 }
@@ -173,7 +175,7 @@ hipError_t launch_kmeans_update(bool xf32, const KmeansParams& p, int n_blocks, 
     LVQ_KM(32, 2) LVQ_KM(32, 4) LVQ_KM(32, 8)
 #undef LVQ_KM
   }
-  hipLaunchKernelGGL(kmeans_finalize_kernel, dim3(n_streams), dim3(256), 0, s, p, G);
+  hipLaunchKernelGGL(kmeans_finalize_kernel, dim3(n_streams), dim3(1024), 0, s, p, G);
   return hipGetLastError();
 }
 
