@@ -522,7 +522,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path is not sharded "
-              "across GPUs in this build", file=sys.stderr)
+              "across GPUs", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

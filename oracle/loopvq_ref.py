@@ -13,7 +13,7 @@ Sources ("the pages"):
 P1's display equations were lost when the page was extracted; where this
 module rebuilds one from the prose it says which sentence it follows.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * channel group g covers the contiguous channels [g*c, (g+1)*c) at every loop
     step of the block (P1 section "Preliminaries", "Vector quantization of the KV cache": G
     contiguous channels; no permutation outside TaSQ);

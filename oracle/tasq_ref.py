@@ -14,13 +14,14 @@ Sources ("the pages"):
   [P2] The jaehun.me summary post of the same paper, section 3.3 "Combining
        with TaSQ" and its restatement of Fig. 2c.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * eq. (10): u = P(w (.) k / sigma_j): the pre-RoPE key of loop step t, head
     h and token j is weighted channel-wise by w^(t)_h, divided by the token's
     scale sigma^(t)_j and permuted by P_{beta,h} of its block;
   * sigma^(t)_j = RMS of w (.) k over all heads and channels of token j at
     step t (P1 "Formulation"), stored in fp16 (P1 "Calibration and
-    bitwidth": 16/(HD) bits per key element).  The fp16-rounded value (round
+    bitwidth" counts it as 16/(H*D) bits of overhead per key element).  The
+    fp16-rounded value (round
     to nearest even) is the one used on both sides: to form u and to rebuild
     the key.  A token whose fp16 sigma is 0 gets u = 0;
   * P keeps each RoPE pair {f, f + D/2} together and places whole pairs in a
@@ -31,7 +32,7 @@ Readings taken where the pages are silent (each also listed in the design doc):
     [g*c, (g+1)*c)), so a code covers c/2 whole RoPE pairs at Tc loop steps;
   * at decode the key is rebuilt in u space from the slice of its step, then
     k_hat = sigma * P^-1(u_hat) / w, then RoPE at the token's position;
-  * Fig. 2c: "the same number of codebooks" is read as one codebook per
+  * Fig. 2c compares the groupings at an equal number of codebooks, read as one codebook per
     (head, K|V, block) under both groupings: the channel grouping codes G
     channels of each of the Tc steps with one codebook shared by the steps,
     the loop grouping codes G/Tc channels at the Tc steps (eq. (4)).  k-means
