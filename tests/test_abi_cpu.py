@@ -301,3 +301,26 @@ def test_rope_table_validation(L):
     assert lib.loopvq_rope_table(4, 96, 1e4, FAKE) == -1
     assert lib.loopvq_rope_table(4, 128, 1e4, None) == -1
     assert lib.loopvq_rope_table(0, 128, 1e4, None) == 0
+
+
+def test_binding_takes_device_tensors_only(L):
+    # the binding has no host path: host tensors are refused before any call
+    import torch
+    d = _dims(L)
+    B, N = 1, 64
+    q = torch.zeros((B, 16, 128), dtype=torch.bfloat16)
+    cache = torch.zeros((1, 16, 2, 64, 32), dtype=torch.uint8)
+    slices = torch.zeros((4, 16, 2, 256, 4), dtype=torch.float16)
+    rope = torch.zeros(64 * 128, dtype=torch.float32)
+    bt = torch.zeros((B, 1), dtype=torch.int32)
+    sl = torch.full((B,), N, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.loopvq_decode_attn(d, 1, q, cache, slices, rope, bt, sl, N, max_pos=64)
+
+
+def test_missing_library_fails_loudly(L, monkeypatch, tmp_path):
+    from decode_attention_loopvq_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libloopvq.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="is missing"):
+        _lib.lib()
