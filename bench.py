@@ -524,6 +524,8 @@ def main():
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path is not sharded "
               "across GPUs", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
 
     import numpy as np
     import torch

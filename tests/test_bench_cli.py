@@ -29,3 +29,9 @@ def test_no_gpu_no_number():
     assert r.returncode == 1
     assert "needs an MI355X GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_zero_steps_is_refused():
+    r = _run("--steps", "0")
+    assert r.returncode == 2
+    assert "--steps must be at least 1" in r.stderr
