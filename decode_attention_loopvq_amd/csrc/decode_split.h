@@ -157,26 +157,45 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      256-byte row (one copy per bank window): entry e of region kv sits
   //      at kv*KENT*256 + e*256, and lane l reads window l % NWIN, so the
   //      random gathers of a wave hit every bank once per pass
+  // Each thread's loads are all issued before its LDS stores (fixed trip
+  // counts, unrolled): a load-store loop waits one L2 round trip per pass.
+  constexpr int NTHR = WAVES * 64;
   if constexpr (PG) {
     // one codebook per channel group: the head's [2][N][KENT] entries as they
     // are (random gathers then meet bank conflicts; 256-byte replication of
     // N*KENT entries would not fit in LDS)
+    constexpr int NV = LDS_SLICES / 16, BATCH = 8;
+    static_assert(NV % (NTHR * BATCH) == 0, "slice copy: whole batches per thread");
     const uint4v* src = (const uint4v*)((const uint8_t*)p.slices + (size_t)h * LDS_SLICES);
-    for (int x = threadIdx.x; x < LDS_SLICES / 16; x += blockDim.x) ((uint4v*)lds)[x] = src[x];
+    for (int x0 = 0; x0 < NV; x0 += NTHR * BATCH) {
+      uint4v v[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) v[j] = src[x0 + j * NTHR + threadIdx.x];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) ((uint4v*)lds)[x0 + j * NTHR + threadIdx.x] = v[j];
+    }
   } else {
+    // 16 threads per entry, one 16-byte piece of its 256-byte row each
+    constexpr int NIT = 2 * KENT * 16 / NTHR;
+    static_assert(2 * KENT * 16 == NIT * NTHR, "slice copy: whole passes per thread");
     const uint8_t* src = (const uint8_t*)p.slices + (size_t)h * 2 * KENT * EB;
-    for (int x = threadIdx.x; x < 2 * KENT * 16; x += blockDim.x) {
-      const int ke = x >> 4, cchunk = x & 15;           // ke = kv * KENT + e
+    uint4v v[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int ke = (it * NTHR + (int)threadIdx.x) >> 4;   // ke = kv * KENT + e
       const uint8_t* sp = src + (size_t)ke * EB;
-      uint4v v;
       if constexpr (EB == 16) {
-        v = *(const uint4v*)sp;
+        v[it] = *(const uint4v*)sp;
       } else if constexpr (EB == 8) {
-        uint2v t = *(const uint2v*)sp; v = (uint4v){t.x, t.y, t.x, t.y};
+        uint2v t = *(const uint2v*)sp; v[it] = (uint4v){t.x, t.y, t.x, t.y};
       } else {
-        uint32_t t = *(const uint32_t*)sp; v = (uint4v){t, t, t, t};
+        uint32_t t = *(const uint32_t*)sp; v[it] = (uint4v){t, t, t, t};
       }
-      *(uint4v*)(lds + ke * 256 + cchunk * 16) = v;
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int x = it * NTHR + (int)threadIdx.x;
+      *(uint4v*)(lds + (x >> 4) * 256 + (x & 15) * 16) = v[it];
     }
   }
   if constexpr (TQ) {
