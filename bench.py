@@ -74,6 +74,25 @@ def _cpu_info():
     return model, os.cpu_count()
 
 
+CLOCK_SETTLE_S = 0.25
+
+
+def settle(fn, torch, seconds: float = CLOCK_SETTLE_S):
+    """Run fn(i) back to back for about `seconds` before a timed region.
+
+    The GPU raises its clocks only after tens of milliseconds of continuous
+    work; a leg whose warm-up steps last a millisecond or two would otherwise
+    time its steps at a clock that is still ramping.  Untimed."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def build_cache(cfg, lv, dims, layer_cb, layer_hsq, lens, bt_np, num_pages, seed, torch, synth):
     """Encode every request's synthetic K/V (all blocks) into a fresh paged cache on the GPU."""
     cache = torch.zeros((cfg.n_blocks, num_pages, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes),
@@ -123,7 +142,7 @@ def bench_decode(args, torch, np, synth, lv):
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    settle(step, torch)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -188,7 +207,7 @@ def bench_window(args, torch, np, synth, lv, dec, n_sink=64, n_recent=256):
                                      workspace=wsp, max_pos=max_seq_len)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    settle(step, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
@@ -223,7 +242,7 @@ def bench_per_group(args, torch, np, synth, lv, dec):
                                dec["seq"], max_seq_len, ws, max_pos=max_seq_len)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    settle(step, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
@@ -260,7 +279,7 @@ def bench_tasq(args, torch, np, synth, lv, dec):
                                    workspace=wsp, max_pos=max_seq_len)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    settle(step, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
@@ -296,7 +315,8 @@ def bench_tasq(args, torch, np, synth, lv, dec):
     reps = max(3, args.steps // 4)
     for _ in range(2):
         lv.loopvq_encode_tasq(edims, xk, xv, ew, eperm, esig, cb, hsq, slots, cache, workspace=ews)
-    torch.cuda.synchronize()
+    settle(lambda i: lv.loopvq_encode_tasq(edims, xk, xv, ew, eperm, esig, cb, hsq, slots, cache, workspace=ews),
+           torch)
     e0.record()
     for _ in range(reps):
         lv.loopvq_encode_tasq(edims, xk, xv, ew, eperm, esig, cb, hsq, slots, cache, workspace=ews)
@@ -340,7 +360,7 @@ def bench_kmeans(args, torch, np, synth, lv):
     slices_buf = torch.empty((cfg.T, cfg.H_kv, 2, cfg.K, cfg.c), dtype=torch.float16, device="cuda")
     iteration(cb, cb2)
     iteration(cb2, cb)
-    torch.cuda.synchronize()
+    settle(lambda i: iteration(cb if i % 2 == 0 else cb2, cb2 if i % 2 == 0 else cb), torch)
     reps = max(3, args.steps // 8)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     eu0, eu1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -381,7 +401,7 @@ def bench_page_encode(args, torch, np, synth, lv, dec):
     _, hsq = lv.loopvq_build_codebook_slices(dims, dec["cb"])
     for _ in range(args.warmup):
         lv.loopvq_encode_pages(dims, pool, src, dec["cb"], hsq, slots, cache)
-    torch.cuda.synchronize()
+    settle(lambda i: lv.loopvq_encode_pages(dims, pool, src, dec["cb"], hsq, slots, cache), torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -412,7 +432,7 @@ def bench_encode(args, torch, np, synth, lv):
     reps = max(3, args.steps // 4)
     for _ in range(2):
         lv.loopvq_encode(dims, xk, xv, cb, hsq, slots, cache)
-    torch.cuda.synchronize()
+    settle(lambda i: lv.loopvq_encode(dims, xk, xv, cb, hsq, slots, cache), torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -566,13 +586,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 q/out; fp16 MFMA operands (codebooks, q, p); fp32 accumulate and RoPE",
         "data": "synthetic (loop-correlated Gaussian K/V encoded on the GPU; fp16 codebooks from a "
                 "synthetic calibration set; bf16 queries)",
         "config": {"workload": f"{cfg.name}: decode attention, B={len(dec['lens'])}, N={dec['max_seq_len']}, "
                                f"H_kv=H_q={cfg.H_kv}, D={cfg.D}, c={cfg.c}, Tc={cfg.Tc}, K={cfg.K} (8-bit), "
                                f"P={cfg.page_size}, one loop step per call, t cycling 1..4",
                    "global_batch": len(dec["lens"]), "seq_len": dec["max_seq_len"], "parallelism": "none (1 GPU)"},
+        "clock_settle_s_per_leg": CLOCK_SETTLE_S,
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "decode_split_ms": round(dec["split_avg_ms"], 5),

@@ -90,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.loopvq_rope_table_floats.restype = ctypes.c_size_t
         L.loopvq_rope_table_floats.argtypes = [I, I]
         L.loopvq_encode.restype = ctypes.c_int
-        L.loopvq_encode.argtypes = [D, I, I, I, P, P, P, P, P, P, ctypes.c_int64, P]
+        L.loopvq_encode.argtypes = [D, I, I, I, P, P, P, P, P, P, ctypes.c_int64, P, P]
         L.loopvq_encode_pages.restype = ctypes.c_int
         L.loopvq_encode_pages.argtypes = [D, I, I, I, P, ctypes.c_int64, P, P, P, P, P, ctypes.c_int64, P]
         L.loopvq_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -154,6 +154,49 @@ def _need(t: torch.Tensor, dtype, name: str, device: bool = True):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _io_dtype(dims: loopvq_dims):
+    return torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
+
+
+def _decode_inputs(dims: loopvq_dims, q: torch.Tensor, index_cache: torch.Tensor, slices: torch.Tensor,
+                   rope_table: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                   max_pos: Optional[int]) -> int:
+    """Dtype, placement and shape checks shared by the decode calls; returns B."""
+    _need(q, _io_dtype(dims), "q"); _need(index_cache, torch.uint8, "index_cache")
+    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
+    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
+    if q.dim() != 3 or tuple(q.shape[1:]) != (dims.H_q, dims.D):
+        raise ValueError(f"q must be [B][{dims.H_q}][{dims.D}], got {tuple(q.shape)}")
+    B = q.shape[0]
+    if seq_lens.numel() < B:
+        raise ValueError(f"seq_lens holds {seq_lens.numel()} entries for {B} requests")
+    if block_table.dim() != 2 or block_table.shape[0] < B:
+        raise ValueError("block_table must be [B][max_pages]")
+    if max_pos is None:
+        raise ValueError("max_pos (positions covered by rope_table) is required")
+    if rope_table.numel() < int(lib().loopvq_rope_table_floats(int(max_pos), int(dims.D))):
+        raise ValueError(f"rope_table holds {rope_table.numel()} floats, fewer than {max_pos} positions need")
+    return B
+
+
+def _decode_outputs(dims: loopvq_dims, B: int, out: torch.Tensor, lse: Optional[torch.Tensor]) -> None:
+    _need(out, _io_dtype(dims), "out")
+    if tuple(out.shape) != (B, dims.H_q, dims.D):
+        raise ValueError(f"out must be [{B}][{dims.H_q}][{dims.D}], got {tuple(out.shape)}")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+        if tuple(lse.shape) != (B, dims.H_q):
+            raise ValueError(f"lse must be [{B}][{dims.H_q}], got {tuple(lse.shape)}")
+
+
+def _workspace(dims: loopvq_dims, B: int, max_seq_len: int, workspace: Optional[torch.Tensor], device):
+    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
+    if workspace is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    _need(workspace, torch.uint8, "workspace")
+    return workspace
+
+
 def loopvq_status_string(status: int) -> str:
     return lib().loopvq_status_string(int(status)).decode()
 
@@ -189,16 +232,23 @@ def loopvq_rope_table(max_pos: int, D: int, base: float = 10000.0) -> torch.Tens
 def loopvq_encode(dims: loopvq_dims, xk: torch.Tensor, xv: torch.Tensor, cb: torch.Tensor,
                   hsq: torch.Tensor, slot_mapping: torch.Tensor, index_cache: torch.Tensor,
                   first_block: int = 0, n_blocks: Optional[int] = None,
-                  block_stride_bytes: Optional[int] = None) -> None:
+                  block_stride_bytes: Optional[int] = None,
+                  near_tie_count: Optional[torch.Tensor] = None) -> None:
     """Encode xk, xv [n_blocks*Tc][n_tok][H_kv][D] into index_cache (uint8).
 
     cb / hsq hold all blocks of the layer; index_cache holds the cache of
     `first_block` first, the next block `block_stride_bytes` later.
+    near_tie_count: None, or a device int32 tensor whose first element the
+    call adds its near-tie count to (the caller zeroes it).
     """
     xdt = torch.float32 if dims.x_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
     _need(xk, xdt, "xk"); _need(xv, xdt, "xv")
     _need(cb, torch.float16, "cb"); _need(hsq, torch.float32, "hsq")
     _need(slot_mapping, torch.int32, "slot_mapping"); _need(index_cache, torch.uint8, "index_cache")
+    if near_tie_count is not None:
+        _need(near_tie_count, torch.int32, "near_tie_count")
+        if near_tie_count.numel() < 1:
+            raise ValueError("near_tie_count must hold one element")
     if n_blocks is None:
         n_blocks = xk.shape[0] // dims.Tc
     n_tok = xk.shape[1]
@@ -208,7 +258,7 @@ def loopvq_encode(dims: loopvq_dims, xk: torch.Tensor, xv: torch.Tensor, cb: tor
         block_stride_bytes = index_cache.numel() // max(n_blocks, 1) if n_blocks > 1 else 0
     _check(lib().loopvq_encode(ctypes.byref(dims), n_tok, first_block, n_blocks, _ptr(xk), _ptr(xv),
                                _ptr(cb), _ptr(hsq), _ptr(slot_mapping), _ptr(index_cache),
-                               int(block_stride_bytes), _stream()), "loopvq_encode")
+                               int(block_stride_bytes), _ptr(near_tie_count), _stream()), "loopvq_encode")
 
 
 def loopvq_encode_pages(dims: loopvq_dims, kv_pages: torch.Tensor, src_slot: torch.Tensor, cb: torch.Tensor,
@@ -243,22 +293,12 @@ def loopvq_decode_attn(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: 
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, max_pos: Optional[int] = None):
     """Decode attention at loop step t; returns (out [B][H_q][D], lse [B][H_q] or None)."""
-    iodt = torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
-    _need(q, iodt, "q"); _need(index_cache, torch.uint8, "index_cache")
-    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
-    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
-    B = q.shape[0]
+    B = _decode_inputs(dims, q, index_cache, slices, rope_table, block_table, seq_lens, max_pos)
     if out is None:
-        out = torch.empty((B, dims.H_q, dims.D), dtype=iodt, device=q.device)
-    _need(out, iodt, "out")
-    if lse is not None:
-        _need(lse, torch.float32, "lse")
-    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if max_pos is None:
-        raise ValueError("max_pos (positions covered by rope_table) is required")
-    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+        out = torch.empty((B, dims.H_q, dims.D), dtype=_io_dtype(dims), device=q.device)
+    _decode_outputs(dims, B, out, lse)
+    workspace = _workspace(dims, B, max_seq_len, workspace, q.device)
+    max_pages = block_table.shape[1]
     _check(lib().loopvq_decode_attn(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
                                     _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
                                     int(max_pages), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
@@ -272,9 +312,9 @@ def loopvq_decode_split(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache:
                         seq_lens: torch.Tensor, max_seq_len: int, workspace: torch.Tensor,
                         sm_scale: float = 0.0, max_pos: Optional[int] = None) -> None:
     """Split-K pass of decode attention; partials are left in `workspace`."""
-    if max_pos is None:
-        raise ValueError("max_pos (positions covered by rope_table) is required")
-    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+    _decode_inputs(dims, q, index_cache, slices, rope_table, block_table, seq_lens, max_pos)
+    _need(workspace, torch.uint8, "workspace")
+    max_pages = block_table.shape[1]
     _check(lib().loopvq_decode_split(ctypes.byref(dims), int(t), q.shape[0], _ptr(q), _ptr(index_cache),
                                      _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
                                      int(max_pages), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
@@ -285,6 +325,10 @@ def loopvq_decode_combine(dims: loopvq_dims, B: int, seq_lens: torch.Tensor, max
                           workspace: torch.Tensor, out: torch.Tensor,
                           lse: Optional[torch.Tensor] = None) -> None:
     """Merge the split partials in `workspace` into out (and lse)."""
+    _need(seq_lens, torch.int32, "seq_lens"); _need(workspace, torch.uint8, "workspace")
+    if seq_lens.numel() < B:
+        raise ValueError(f"seq_lens holds {seq_lens.numel()} entries for {B} requests")
+    _decode_outputs(dims, int(B), out, lse)
     _check(lib().loopvq_decode_combine(ctypes.byref(dims), int(B), _ptr(seq_lens), int(max_seq_len), _ptr(out),
                                        _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream()),
            "loopvq_decode_combine")
@@ -303,24 +347,16 @@ def loopvq_decode_attn_window(dims: loopvq_dims, t: int, q: torch.Tensor, index_
     [B][max_pages] int32 (bf16 token u of a request in page u // 8, slot u % 8);
     n_sink, win_start [B] int32.  Returns (out, lse).
     """
-    iodt = torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
-    _need(q, iodt, "q"); _need(index_cache, torch.uint8, "index_cache")
-    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
-    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
+    B = _decode_inputs(dims, q, index_cache, slices, rope_table, block_table, seq_lens, max_pos)
     _need(kv_bf16, torch.bfloat16, "kv_bf16"); _need(page_table, torch.int32, "page_table")
     _need(n_sink, torch.int32, "n_sink"); _need(win_start, torch.int32, "win_start")
-    B = q.shape[0]
+    if n_sink.numel() < B or win_start.numel() < B or page_table.dim() != 2 or page_table.shape[0] < B:
+        raise ValueError("n_sink, win_start need B entries and page_table B rows")
     if out is None:
-        out = torch.empty((B, dims.H_q, dims.D), dtype=iodt, device=q.device)
-    _need(out, iodt, "out")
-    if lse is not None:
-        _need(lse, torch.float32, "lse")
-    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if max_pos is None:
-        raise ValueError("max_pos (positions covered by rope_table) is required")
-    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+        out = torch.empty((B, dims.H_q, dims.D), dtype=_io_dtype(dims), device=q.device)
+    _decode_outputs(dims, B, out, lse)
+    workspace = _workspace(dims, B, max_seq_len, workspace, q.device)
+    max_pages = block_table.shape[1]
     win = loopvq_bf16_window(kv_bf16.data_ptr(), page_table.data_ptr(),
                              page_table.shape[1] if page_table.dim() == 2 else 0,
                              n_sink.data_ptr(), win_start.data_ptr())
@@ -382,31 +418,22 @@ def loopvq_decode_attn_tasq(dims: loopvq_dims, t: int, q: torch.Tensor, index_ca
                             workspace: Optional[torch.Tensor] = None, max_pos: Optional[int] = None):
     """Decode attention at loop step t over TaSQ-coded keys; window = (kv_bf16, page_table, n_sink,
     win_start) adds the bf16 sink and recent window.  Returns (out, lse)."""
-    iodt = torch.float32 if dims.io_dtype == LOOPVQ_DTYPE_F32 else torch.bfloat16
-    _need(q, iodt, "q"); _need(index_cache, torch.uint8, "index_cache")
-    _need(slices, torch.float16, "slices"); _need(rope_table, torch.float32, "rope_table")
-    _need(block_table, torch.int32, "block_table"); _need(seq_lens, torch.int32, "seq_lens")
+    B = _decode_inputs(dims, q, index_cache, slices, rope_table, block_table, seq_lens, max_pos)
     tq = _tasq_struct(dims, w, perm, sigma)
-    B = q.shape[0]
     if out is None:
-        out = torch.empty((B, dims.H_q, dims.D), dtype=iodt, device=q.device)
-    _need(out, iodt, "out")
-    if lse is not None:
-        _need(lse, torch.float32, "lse")
-    need = loopvq_decode_workspace_bytes(dims, B, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if max_pos is None:
-        raise ValueError("max_pos (positions covered by rope_table) is required")
+        out = torch.empty((B, dims.H_q, dims.D), dtype=_io_dtype(dims), device=q.device)
+    _decode_outputs(dims, B, out, lse)
+    workspace = _workspace(dims, B, max_seq_len, workspace, q.device)
     win = None
     if window is not None:
         kv_bf16, page_table, n_sink, win_start = window
         _need(kv_bf16, torch.bfloat16, "kv_bf16"); _need(page_table, torch.int32, "page_table")
         _need(n_sink, torch.int32, "n_sink"); _need(win_start, torch.int32, "win_start")
-        win = loopvq_bf16_window(kv_bf16.data_ptr(), page_table.data_ptr(),
-                                 page_table.shape[1] if page_table.dim() == 2 else 0,
+        if n_sink.numel() < B or win_start.numel() < B or page_table.dim() != 2 or page_table.shape[0] < B:
+            raise ValueError("n_sink, win_start need B entries and page_table B rows")
+        win = loopvq_bf16_window(kv_bf16.data_ptr(), page_table.data_ptr(), page_table.shape[1],
                                  n_sink.data_ptr(), win_start.data_ptr())
-    max_pages = block_table.shape[1] if block_table.dim() == 2 else 0
+    max_pages = block_table.shape[1]
     _check(lib().loopvq_decode_attn_tasq(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
                                          _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
                                          int(max_pages), _ptr(seq_lens), int(max_seq_len), ctypes.byref(tq),

@@ -186,7 +186,8 @@ size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D) {
 static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
                        const void* xk, const void* xv, const int32_t* src_slot, int64_t step_stride,
                        const void* cb, const float* hsq, const int32_t* slot_mapping, uint8_t* index_cache,
-                       int64_t block_stride_bytes, int kv_lo, int kv_n, bool xf32, hipStream_t stream) {
+                       int64_t block_stride_bytes, int kv_lo, int kv_n, bool xf32, int32_t* near_tie,
+                       hipStream_t stream) {
   int st = check_dims(dims);
   if (st != LOOPVQ_OK) return st;
   const int nb_total = dims->T / dims->Tc;
@@ -218,6 +219,7 @@ static int encode_impl(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   p.per_group = dims->per_group;
   p.kv_lo = kv_lo;
   p.kv_n = kv_n;
+  p.near_tie = near_tie;
   // units of 32 (token, group) vectors (per group: 32 tokens of one group);
   // about 8192 waves over the whole call
   const long long streams = (long long)n_blocks * kv_n * H * n_codebook_groups(dims);
@@ -237,11 +239,13 @@ extern "C" {
 int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
                   const void* xk, const void* xv, const void* cb, const float* hsq,
                   const int32_t* slot_mapping, uint8_t* index_cache, int64_t block_stride_bytes,
-                  hipStream_t stream) {
+                  int32_t* near_tie_count, hipStream_t stream) {
   if (check_dims(dims) != LOOPVQ_OK) return check_dims(dims);
+  if (((uintptr_t)near_tie_count & 3) != 0) return LOOPVQ_ERR_INVALID_ARG;
   const int64_t step_stride = (int64_t)std::max(n_tok, 0) * dims->H_kv * dims->D;
   return encode_impl(dims, n_tok, first_block, n_blocks, xk, xv, nullptr, step_stride, cb, hsq, slot_mapping,
-                     index_cache, block_stride_bytes, 0, 2, dims->x_dtype == LOOPVQ_DTYPE_F32, stream);
+                     index_cache, block_stride_bytes, 0, 2, dims->x_dtype == LOOPVQ_DTYPE_F32, near_tie_count,
+                     stream);
 }
 
 int loopvq_encode_pages(const loopvq_dims* dims, int32_t n_tok, int32_t first_block, int32_t n_blocks,
@@ -258,7 +262,7 @@ int loopvq_encode_pages(const loopvq_dims* dims, int32_t n_tok, int32_t first_bl
   // block beta of this call reads loop steps (beta - first_block)*Tc .. of the pools
   const void* xv = kv_pages ? (const void*)((const uint16_t*)kv_pages + 8 * dims->D) : nullptr;
   return encode_impl(dims, n_tok, first_block, n_blocks, kv_pages, xv, src_slot, step_stride, cb, hsq,
-                     slot_mapping, index_cache, block_stride_bytes, 0, 2, false, stream);
+                     slot_mapping, index_cache, block_stride_bytes, 0, 2, false, nullptr, stream);
 }
 
 size_t loopvq_encode_tasq_workspace_bytes(const loopvq_dims* dims, int32_t n_tok, int32_t n_blocks) {
@@ -303,10 +307,10 @@ int loopvq_encode_tasq(const loopvq_dims* dims, int32_t n_tok, int32_t first_blo
   const int64_t step_stride = (int64_t)n_tok * dims->H_kv * dims->D;
   // keys: the codes of u (fp32); values: as loopvq_encode
   st = encode_impl(dims, n_tok, first_block, n_blocks, workspace, workspace, nullptr, step_stride, cb, hsq,
-                   slot_mapping, index_cache, block_stride_bytes, 0, 1, true, stream);
+                   slot_mapping, index_cache, block_stride_bytes, 0, 1, true, nullptr, stream);
   if (st != LOOPVQ_OK) return st;
   return encode_impl(dims, n_tok, first_block, n_blocks, xv, xv, nullptr, step_stride, cb, hsq, slot_mapping,
-                     index_cache, block_stride_bytes, 1, 1, dims->x_dtype == LOOPVQ_DTYPE_F32, stream);
+                     index_cache, block_stride_bytes, 1, 1, dims->x_dtype == LOOPVQ_DTYPE_F32, nullptr, stream);
 }
 
 size_t loopvq_kmeans_workspace_bytes(const loopvq_dims* dims, int32_t n_blocks) {

@@ -28,6 +28,11 @@
 //    the raw input loads run three units ahead of the scoring.
 //  * The argmax is exact, so it costs VALU work per score (a three-input max
 //    per two scores); that VALU work, not the MFMA rate, bounds the kernel.
+//  * Near-tie count (NTC, only when the caller asks for it): a vector is a near
+//    tie when a second entry scores within 0.5e-6*(||z||^2 + ||e_a||^2) of the
+//    best (squared distances within 1e-6 of that scale).  The instance that
+//    counts them rescores the vector's tiles after the search and adds the
+//    wave's count to one device counter; the plain instance carries none of it.
 
 #include <type_traits>
 
@@ -36,7 +41,7 @@
 
 namespace loopvq {
 
-template <int G, int C, bool XF32, int BITS, bool PAGED, bool PG>
+template <int G, int C, bool XF32, int BITS, bool PAGED, bool PG, bool NTC>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   constexpr int KD = XF32 ? 2 * G : G;          // reduction length (fp32: high and low halves)
   constexpr int KDP = KD < 16 ? 16 : KD;        // padded to the MFMA depth
@@ -293,11 +298,38 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     for (int r = 14; r >= 0; --r) rr = bd[r] == best ? r : rr;
     int bidx = 32 * btile + 8 * (rr >> 2) + 4 * hf + (rr & 3);
     // ---- merge the two lanes holding the same vector (lower index on ties)
+    const float ob = __shfl_xor(best, 32);
     {
-      const float ob = __shfl_xor(best, 32);
       const int oi = __shfl_xor(bidx, 32);
       const bool take = ob > best || (ob == best && oi < bidx);
       bidx = take ? oi : bidx;
+    }
+    if constexpr (NTC) {
+      // near tie: some entry other than the chosen one scores at least
+      // best - 0.5e-6*(||z||^2 + ||e_a||^2), i.e. two or more entries do.
+      // ||z||^2 from the lane's operand half (fp32 input: the high parts)
+      float zz = 0.f;
+#pragma unroll
+      for (int mu = 0; mu < NMF; ++mu)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kap = 16 * mu + 8 * hf + j;
+          if (kap < G) zz = fmaf((float)Bv[mu][j], (float)Bv[mu][j], zz);
+        }
+      zz += __shfl_xor(zz, 32);
+      // 0.5*||e_a||^2 sits at hsl[t][h][q][s] for entry a = 32t + 8q + 4h + s
+      const int hx = ((bidx >> 5) << 5) | (((bidx >> 2) & 1) << 4) | (((bidx >> 3) & 3) << 2) | (bidx & 3);
+      const float thr = __builtin_fmaxf(best, ob) - 0.5e-6f * (zz - 2.f * hsl[hx]);
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        const float16v d = tile_scores(t);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cnt += d[r] >= thr ? 1 : 0;
+      }
+      cnt += __shfl_xor(cnt, 32);
+      const uint64_t tied = __ballot(hf == 0 && vok && cnt >= 2);
+      if (lane == 0 && tied != 0) atomicAdd(p.near_tie, (int)__popcll(tied));
     }
     // ---- write the code into its row slot
     // byte of the code: page, row in the page (rows are a power of two of
@@ -329,14 +361,18 @@ template <int G, int C, bool XF32, int BITS, bool PG>
 static hipError_t launch_encode_pg(const EncodeParams& p, int n_blocks, hipStream_t s) {
   dim3 grid(p.n_unit_groups, n_blocks * p.kv_n * p.H_kv * (PG ? p.D / C : 1));
   if constexpr (!XF32) {
-    // bf16 window pages (decode-time page encoding)
+    // bf16 window pages (decode-time page encoding); no near-tie count there
     if (p.src_slot != nullptr) {
-      hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true, PG>), grid, dim3(256), 0, s, p);
+      if (p.near_tie != nullptr) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true, PG, false>), grid, dim3(256), 0, s, p);
       return hipGetLastError();
     }
   }
   if (p.src_slot != nullptr) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG>), grid, dim3(256), 0, s, p);
+  if (p.near_tie != nullptr)
+    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -80,6 +80,7 @@ struct EncodeParams {
   int kv_lo, kv_n;            // code streams kv_lo .. kv_lo + kv_n - 1 of {K, V}
   int units_per_wave;         // units of 32 consecutive (token, group) vectors per wave
   int n_unit_groups;          // ceil(units / (4 * units_per_wave)), the grid's x extent
+  int32_t* near_tie;          // device counter the near-tie count is added to, or null
 };
 
 // TaSQ key transform: u = P(w k / sigma) and the fp16 sigma of every token

@@ -86,7 +86,7 @@ typedef struct loopvq_dims {
   int32_t K;          /* codebook entries, must equal 1 << bits                         */
   int32_t H_kv;       /* KV heads                                                       */
   int32_t H_q;        /* query heads, a multiple of H_kv                                */
-  int32_t page_size;  /* tokens per page P: a power of two in [16, 256]                 */
+  int32_t page_size;  /* tokens per page P: a power of two in [8, 1024]                 */
   int32_t x_dtype;    /* encoder input K/V: LOOPVQ_DTYPE_F32 or LOOPVQ_DTYPE_BF16        */
   int32_t io_dtype;   /* decode query and output: LOOPVQ_DTYPE_F32 or LOOPVQ_DTYPE_BF16  */
   int32_t per_group;  /* 0: one codebook per (block, KV head, K|V), shared by the D/c
@@ -155,17 +155,26 @@ size_t loopvq_rope_table_floats(int32_t max_pos, int32_t D);
  *                 outside the cache writes outside it).
  *   index_cache   cache of block first_block; block beta's cache starts at
  *                 index_cache + (beta - first_block)*block_stride_bytes.
+ *   near_tie_count  NULL, or one device int32 (4-byte aligned) to which the
+ *                 call adds the number of coupled vectors it coded whose two
+ *                 smallest distances lie within 1e-6*(||z||^2 + ||e_a||^2) of
+ *                 each other (e_a the chosen entry), as judged on the fp32
+ *                 scores the encoder computes; exact ties (duplicate entries)
+ *                 always count.  The caller zeroes it.  NULL runs the plain
+ *                 encoder, which does no near-tie work; a count costs a
+ *                 second scoring pass over the codebook.
  * Distances are evaluated as ||z||^2 - 2 z.e + ||e||^2 with fp16 inputs and
  * fp32 accumulation (bf16 inputs convert exactly to fp16 inside fp16's normal
  * range; fp32 inputs are split into two fp16 terms), so the index can differ
  * from an exact evaluation only where two distances lie within fp32 rounding
- * of each other.
+ * of each other.  Entries whose fp16 values are identical score identically,
+ * and the lowest of their indices is the one written.
  */
 int loopvq_encode(const loopvq_dims* dims, int32_t n_tok, int32_t first_block,
                   int32_t n_blocks, const void* xk, const void* xv,
                   const void* cb, const float* hsq, const int32_t* slot_mapping,
                   uint8_t* index_cache, int64_t block_stride_bytes,
-                  hipStream_t stream);
+                  int32_t* near_tie_count, hipStream_t stream);
 
 /*
  * Decode-time page encoding: code tokens held in bf16 pages (the recent
@@ -207,6 +216,12 @@ size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
  * their logsumexp, which recovers the exact softmax.]
  *   t             loop step, 1 <= t <= T; reads block (t-1)/Tc, slice t-1.
  *   q             [B][H_q][D] queries already rotated at their own position.
+ *                 bf16 queries enter the matrix cores as fp16 values, so
+ *                 every |q_i| must stay below 65504 (fp16's largest finite
+ *                 value; larger values become infinite scores); magnitudes
+ *                 below 2^-14 are rounded to fp16 subnormals (an absolute
+ *                 error below 2^-25).  fp32 queries are carried as two fp16
+ *                 terms and need |q_i| below 65504 as well.
  *   index_cache   the cache of block (t-1)/Tc.
  *   slices        [T][H_kv][2][K][c] fp16 from loopvq_build_codebook_slices.
  *   rope_table    device copy of loopvq_rope_table(max_pos, D, base).

@@ -148,18 +148,23 @@ def test_window_decode_validation_before_launch(L):
 def test_encode_validation_before_launch(L):
     lib = L.lib()
     d = _dims(L)
-    def call(n_tok=10, first=0, nb=1, stride=0, ptr=FAKE):
-        return lib.loopvq_encode(ctypes.byref(d), n_tok, first, nb, ptr, ptr, ptr, ptr, ptr, ptr, stride, None)
+    def call(n_tok=10, first=0, nb=1, stride=0, ptr=FAKE, ties=None):
+        return lib.loopvq_encode(ctypes.byref(d), n_tok, first, nb, ptr, ptr, ptr, ptr, ptr, ptr, stride, ties,
+                                 None)
     assert call(n_tok=-1) == -1
     assert call(first=1) == -1
     assert call(nb=0) == -1
     assert call(nb=2) == -1
     assert call(ptr=None) == -1
     assert call(n_tok=0, ptr=None) == 0
+    assert call(n_tok=0, ptr=None, ties=FAKE) == 0                    # the counter is optional and untouched
+    assert call(ties=ctypes.c_void_p((1 << 20) + 2)) == -1            # near-tie counter not 4-byte aligned
+    assert call(n_tok=-1, ties=FAKE) == -1
     d8 = _dims(L, T=8)
-    assert lib.loopvq_encode(ctypes.byref(d8), 4, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    assert lib.loopvq_encode(ctypes.byref(d8), 4, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -1
     d_small = _dims(L, D=64, c=8, bits=4)  # 8 groups per token: 4-bit rows need a multiple of 16
-    assert lib.loopvq_encode(ctypes.byref(d_small), 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    assert lib.loopvq_encode(ctypes.byref(d_small), 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None,
+                             None) == -2
 
 
 def test_encode_pages_validation_before_launch(L):
@@ -316,6 +321,58 @@ def test_binding_takes_device_tensors_only(L):
     sl = torch.full((B,), N, dtype=torch.int32)
     with pytest.raises(ValueError, match="device tensor"):
         L.loopvq_decode_attn(d, 1, q, cache, slices, rope, bt, sl, N, max_pos=64)
+    ws = torch.zeros(L.loopvq_decode_workspace_bytes(d, B, N), dtype=torch.uint8)
+    out = torch.zeros((B, 16, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.loopvq_decode_split(d, 1, q, cache, slices, rope, bt, sl, N, ws, max_pos=64)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.loopvq_decode_combine(d, B, sl, N, ws, out)
+
+
+def test_binding_checks_shapes_before_the_call(L, monkeypatch):
+    # shape checks of the decode wrappers, with the device-placement check
+    # relaxed so that host tensors reach them; each raises before the library
+    # is asked to launch anything
+    import torch
+    from decode_attention_loopvq_amd import _lib
+
+    def need_anywhere(t, dtype, name, device=True):
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    monkeypatch.setattr(_lib, "_need", need_anywhere)
+    d = _dims(L)
+    B, N = 2, 64
+    q = torch.zeros((B, 16, 128), dtype=torch.bfloat16)
+    cache = torch.zeros((1, 16, 2, 64, 32), dtype=torch.uint8)
+    slices = torch.zeros((4, 16, 2, 256, 4), dtype=torch.float16)
+    rope = torch.zeros(int(L.lib().loopvq_rope_table_floats(64, 128)), dtype=torch.float32)
+    bt = torch.zeros((B, 1), dtype=torch.int32)
+    sl = torch.full((B,), N, dtype=torch.int32)
+    ws = torch.zeros(L.loopvq_decode_workspace_bytes(d, B, N), dtype=torch.uint8)
+    out = torch.zeros((B, 16, 128), dtype=torch.bfloat16)
+    split = lambda **kw: L.loopvq_decode_split(d, 1, kw.get("q", q), cache, slices, kw.get("rope", rope),
+                                               kw.get("bt", bt), kw.get("sl", sl), N, ws,
+                                               max_pos=kw.get("max_pos", 64))
+    with pytest.raises(ValueError, match="q must be"):
+        split(q=torch.zeros((B, 8, 128), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="q: expected"):
+        split(q=torch.zeros((B, 16, 128), dtype=torch.float32))
+    with pytest.raises(ValueError, match="seq_lens"):
+        split(sl=torch.full((1,), N, dtype=torch.int32))
+    with pytest.raises(ValueError, match="block_table"):
+        split(bt=torch.zeros((1, 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="rope_table holds"):
+        split(max_pos=65)
+    with pytest.raises(ValueError, match="rope_table holds"):
+        split(rope=rope[:-1])
+    with pytest.raises(ValueError, match="out must be"):
+        L.loopvq_decode_combine(d, B, sl, N, ws, torch.zeros((B, 16, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse must be"):
+        L.loopvq_decode_combine(d, B, sl, N, ws, out, torch.zeros((B,), dtype=torch.float32))
+    with pytest.raises(ValueError, match="seq_lens"):
+        L.loopvq_decode_combine(d, B + 1, sl, N, ws, torch.zeros((B + 1, 16, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        L.loopvq_decode_attn(d, 1, q, cache, slices, rope, bt, sl, N, out=out[:1], max_pos=64)
 
 
 def test_missing_library_fails_loudly(L, monkeypatch, tmp_path):

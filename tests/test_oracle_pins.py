@@ -158,6 +158,28 @@ def test_pack_round_trip_8bit_and_4bit():
         np.testing.assert_array_equal(oracle.unpack_rows(rows, bits, ng), idx)
 
 
+def test_paged_scatter_gather_hand_worked():
+    # explicit byte positions worked out by hand from the page / head / K|V /
+    # offset strides, so a convention shared by scatter and gather (a swapped
+    # axis, a wrong page lookup) cannot pass by round-tripping
+    g = _golden("paged_rows.json")
+    cache = np.zeros(g["shape"], dtype=np.uint8)
+    for w in g["writes"]:
+        oracle.scatter_rows(cache, np.array(w["rows"], np.uint8), np.array(w["slots"]), w["h"], w["kv"])
+    want = np.zeros(cache.size, dtype=np.uint8)
+    for off, val in g["nonzero_bytes"]:
+        want[off] = val
+    np.testing.assert_array_equal(cache.reshape(-1), want)
+    for gg in g["gathers"]:
+        got = oracle.gather_rows(cache, np.array(gg["block_table"]), gg["n"], gg["h"], gg["kv"])
+        np.testing.assert_array_equal(got, np.array(gg["rows"], np.uint8))
+    for gg in g["gathers_at"]:
+        got = oracle.gather_rows_at(cache, np.array(gg["block_table"]), np.array(gg["pos"]), gg["h"], gg["kv"])
+        np.testing.assert_array_equal(got, np.array(gg["rows"], np.uint8))
+    u = g["unpack_8bit"]
+    np.testing.assert_array_equal(oracle.unpack_rows(np.array(u["rows"], np.uint8), 8, 4), np.array(u["codes"]))
+
+
 def test_paged_scatter_gather_round_trip():
     cfg = synth.config_by_name("tiny").replace(page_size=8)
     lens = np.array([13, 30, 1])
