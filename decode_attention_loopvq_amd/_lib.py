@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_decode_attn.restype = ctypes.c_int
         L.loopvq_decode_attn.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.c_float,
                                          P, P, P, ctypes.c_size_t, P]
+        L.loopvq_decode_attn_noalloc.restype = ctypes.c_int
+        L.loopvq_decode_attn_noalloc.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.c_float, P, P, P]
         L.loopvq_decode_split.restype = ctypes.c_int
         L.loopvq_decode_split.argtypes = [D, I, I, P, P, P, P, I, P, I, P, I, ctypes.c_float, P,
                                           ctypes.c_size_t, P]
@@ -127,7 +129,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("loopvq_status_string", "loopvq_row_bytes", "loopvq_build_codebook_slices",
             "loopvq_rope_table", "loopvq_rope_table_floats", "loopvq_encode", "loopvq_encode_pages",
             "loopvq_decode_workspace_bytes",
-            "loopvq_decode_attn", "loopvq_decode_split", "loopvq_decode_combine",
+            "loopvq_decode_attn", "loopvq_decode_attn_noalloc", "loopvq_decode_split", "loopvq_decode_combine",
             "loopvq_decode_attn_window", "loopvq_encode_tasq_workspace_bytes", "loopvq_encode_tasq",
             "loopvq_decode_attn_tasq", "loopvq_kmeans_workspace_bytes", "loopvq_kmeans_update")
 
@@ -305,6 +307,25 @@ def loopvq_decode_attn(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: 
                                     _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()),
                                     _stream()), "loopvq_decode_attn")
     return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # LOOPVQ_NOALLOC_SCRATCH_BYTES
+
+
+def loopvq_decode_attn_noalloc(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: torch.Tensor,
+                               slices: torch.Tensor, rope_table: torch.Tensor, block_table: torch.Tensor,
+                               seq_lens: torch.Tensor, max_seq_len: int, out: torch.Tensor,
+                               lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0,
+                               max_pos: Optional[int] = None) -> None:
+    """loopvq_decode_attn with its split partials in the library's fixed device scratch: the C call
+    allocates nothing (out and lse are the caller's tensors)."""
+    B = _decode_inputs(dims, q, index_cache, slices, rope_table, block_table, seq_lens, max_pos)
+    _decode_outputs(dims, B, out, lse)
+    _check(lib().loopvq_decode_attn_noalloc(ctypes.byref(dims), int(t), B, _ptr(q), _ptr(index_cache),
+                                            _ptr(slices), _ptr(rope_table), int(max_pos), _ptr(block_table),
+                                            int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                                            float(sm_scale), _ptr(out), _ptr(lse), _stream()),
+           "loopvq_decode_attn_noalloc")
 
 
 def loopvq_decode_split(dims: loopvq_dims, t: int, q: torch.Tensor, index_cache: torch.Tensor,

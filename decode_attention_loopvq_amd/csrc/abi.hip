@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -130,6 +131,7 @@ const char* loopvq_status_string(int status) {
     case LOOPVQ_ERR_UNSUPPORTED: return "unsupported shape, code width or dtype";
     case LOOPVQ_ERR_WORKSPACE: return "workspace too small";
     case LOOPVQ_ERR_HIP: return "HIP runtime or launch error";
+    case LOOPVQ_ERR_SCRATCH: return "batch needs more than the fixed device scratch of the no-allocation decode";
     default: return "unknown status";
   }
 }
@@ -575,6 +577,57 @@ int loopvq_decode_attn_tasq(const loopvq_dims* dims, int32_t t, int32_t B, const
                   nullptr, max_seq_len, sm_scale, workspace, workspace_bytes, tasq, stream);
   if (st != LOOPVQ_OK) return st;
   return combine_impl(dims, B, seq_lens, max_seq_len, out, lse, workspace, workspace_bytes, false, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation decode
+// The split partials of loopvq_decode_attn_noalloc live in this fixed array.
+// Each GPU holds its own copy at its own address; host code never uses the
+// name itself as an address (on the host it is only a stand-in for the
+// symbol), only the device address looked up for the current device.
+static __device__ __align__(256) uint8_t scratch[LOOPVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[SCRATCH_MAX_DEVICES];   // device address of scratch, per device id
+
+// address of the current device's copy, looked up once per device
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return LOOPVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LOOPVQ_ERR_HIP;
+    scratch_dev[dev] = ptr;
+  }
+  *out = scratch_dev[dev];
+  return LOOPVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int loopvq_decode_attn_noalloc(const loopvq_dims* dims, int32_t t, int32_t B, const void* q,
+                               const uint8_t* index_cache, const void* slices, const float* rope_table,
+                               int32_t max_pos, const int32_t* block_table, int32_t max_pages,
+                               const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, void* out,
+                               float* lse, hipStream_t stream) {
+  int st = check_decode_common(dims, B, max_seq_len);
+  if (st != LOOPVQ_OK) return st;
+  if (plan_decode(dims, B, max_seq_len).total() > (size_t)LOOPVQ_NOALLOC_SCRATCH_BYTES) return LOOPVQ_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (B > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st != LOOPVQ_OK) return st;
+  }
+  return loopvq_decode_attn(dims, t, B, q, index_cache, slices, rope_table, max_pos, block_table, max_pages,
+                            seq_lens, max_seq_len, sm_scale, out, lse, ws,
+                            ws != nullptr ? (size_t)LOOPVQ_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 }  // extern "C"

@@ -71,7 +71,8 @@ enum {
   LOOPVQ_ERR_INVALID_ARG = -1,      /* null pointer, inconsistent sizes, bad t, ...     */
   LOOPVQ_ERR_UNSUPPORTED = -2,      /* valid but not compiled: bits, c, D, dtype, ...   */
   LOOPVQ_ERR_WORKSPACE = -3,        /* decode workspace smaller than required           */
-  LOOPVQ_ERR_HIP = -4               /* a HIP launch or runtime call failed              */
+  LOOPVQ_ERR_HIP = -4,              /* a HIP launch or runtime call failed              */
+  LOOPVQ_ERR_SCRATCH = -5           /* batch needs more than the fixed device scratch   */
 };
 
 enum { LOOPVQ_DTYPE_F32 = 0, LOOPVQ_DTYPE_BF16 = 1 };
@@ -270,6 +271,36 @@ int loopvq_decode_combine(const loopvq_dims* dims, int32_t B, const int32_t* seq
                           int32_t max_seq_len, void* out, float* lse,
                           const void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* Bytes of the fixed device scratch of loopvq_decode_attn_noalloc (8 MiB). */
+#define LOOPVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * loopvq_decode_attn for callers that cannot allocate device memory (code
+ * under stream or graph capture, serving loops and harnesses that forbid
+ * hipMalloc): the same kernels and the same result bit for bit, with the
+ * split partials kept in a fixed device array of the library instead of a
+ * caller workspace.  The call allocates nothing.
+ *   Limit: the batch's loopvq_decode_workspace_bytes(dims, B, max_seq_len)
+ *          must not exceed LOOPVQ_NOALLOC_SCRATCH_BYTES, else the call returns
+ *          LOOPVQ_ERR_SCRATCH and enqueues nothing (for example 16 requests of
+ *          32K tokens and 16 heads need 2.2 MiB).
+ *   Scope: each GPU holds one copy of the array, from the first call on that
+ *          device (the call that looks its address up, with the device
+ *          current) until the process ends.  Every call on one GPU uses that
+ *          GPU's copy: calls on one GPU whose work may overlap (other streams,
+ *          other host threads) race on it and must be ordered by the caller.
+ *          Nothing in it needs to start at zero.
+ *   stream must belong to the current device.  Other arguments as for
+ *   loopvq_decode_attn.
+ */
+int loopvq_decode_attn_noalloc(const loopvq_dims* dims, int32_t t, int32_t B,
+                               const void* q, const uint8_t* index_cache,
+                               const void* slices, const float* rope_table,
+                               int32_t max_pos, const int32_t* block_table,
+                               int32_t max_pages, const int32_t* seq_lens,
+                               int32_t max_seq_len, float sm_scale, void* out,
+                               float* lse, hipStream_t stream);
 
 /*
  * The bf16 pages of a request: its attention sink and its recent window.

@@ -42,7 +42,7 @@ def test_header_symbols_exported(L):
 
 
 def test_status_strings(L):
-    for s in (0, -1, -2, -3, -4, 7):
+    for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(L.loopvq_status_string(s), str) and L.loopvq_status_string(s)
 
 
@@ -306,6 +306,23 @@ def test_rope_table_validation(L):
     assert lib.loopvq_rope_table(4, 96, 1e4, FAKE) == -1
     assert lib.loopvq_rope_table(4, 128, 1e4, None) == -1
     assert lib.loopvq_rope_table(0, 128, 1e4, None) == 0
+
+
+def test_noalloc_decode_rejects_batches_beyond_its_scratch(L):
+    # checked on the host before the scratch address is looked up or anything
+    # is launched, so it needs no GPU
+    lib = L.lib()
+    d = _dims(L)
+    def call(B, n, ptr=FAKE):
+        return lib.loopvq_decode_attn_noalloc(ctypes.byref(d), 1, B, ptr, ptr, ptr, ptr, n, ptr, 1 << 12, ptr, n,
+                                              0.0, ptr, ptr, None)
+    cap = 8 << 20
+    assert L.loopvq_decode_workspace_bytes(d, 16, 32768) <= cap          # the 32K batch fits
+    assert L.loopvq_decode_workspace_bytes(d, 256, 65536) > cap
+    assert call(256, 65536) == -5
+    assert "scratch" in L.loopvq_status_string(-5)
+    assert call(0, 64, ptr=None) == 0                                     # empty batch: nothing to do
+    assert call(-1, 64) == -1
 
 
 def test_binding_takes_device_tensors_only(L):
