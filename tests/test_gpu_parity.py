@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (GpuLayer, check_codes, compare, dims_for, io_tensor, make_cache_from_data, ref_decode,
-                      to_dev, x_tensor)
+from gpu_util import (GpuLayer, bound, check_codes, compare, dims_for, io_tensor, make_cache_from_data,
+                      ref_decode, to_dev, x_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +134,55 @@ def test_full_size_decode_sampled(name, t_list, requests, heads):
         err, ratio = compare(cfg, o, lse, ref, lens)
         _note(f"{name} decode t={t}: max err {err:.2e} (bound ratio {ratio:.2f})")
         assert ratio <= 1.0
+
+
+def test_gpu_encoded_32k_cache_sampled():
+    # the 32K batch as bench.py builds and times it: keys and values drawn on
+    # the GPU (torch's generator), coded by the GPU encoder, decoded by the GPU.
+    # For sampled (request, head) streams the oracle encodes the same values
+    # itself (the GPU's codes must be its codes outside the near-tie band) and
+    # decodes its own cache; the GPU's output on the GPU-coded cache must match
+    # that within the output bound.
+    cfg = synth.config_by_name("longctx32k")
+    lens = synth.make_seq_lens(cfg)
+    bt, npg = synth.make_block_table(cfg, lens)
+    cb = synth.make_codebooks(cfg)
+    layer = GpuLayer(cfg, cb, int(lens.max()))
+    cache = torch.zeros((npg, cfg.H_kv, 2, cfg.page_size, cfg.row_bytes), dtype=torch.uint8, device="cuda")
+    sample = {0: (3, 12), 9: (0,)}
+    host_kv = {}
+    for b, n in enumerate(lens):
+        xk, xv = synth.make_kv_torch(cfg, int(n), cfg.index * 1000 + b)
+        slots = to_dev(synth.slot_mapping_for(bt, b, int(n), cfg.page_size))
+        lv.loopvq_encode(layer.dims, xk, xv, layer.cb, layer.hsq, slots, cache)
+        for h in sample.get(b, ()):
+            host_kv[(b, h)] = (xk[:, :, h:h + 1].float().cpu().numpy(), xv[:, :, h:h + 1].float().cpu().numpy())
+        del xk, xv
+    torch.cuda.synchronize()
+    got_cache = cache.cpu().numpy()
+    t = 3
+    q = synth.make_queries(cfg, len(lens), t=t)
+    o, lse = layer.decode(t, q, cache, bt, lens)
+    grp = cfg.H_q // cfg.H_kv
+    for (b, h), (xk, xv) in host_kv.items():
+        n = int(lens[b])
+        slots = synth.slot_mapping_for(bt, b, n, cfg.page_size)
+        ref_cache, ties, results = oracle.build_index_cache(xk, xv, cb[:, h:h + 1], cfg.Tc, cfg.c, cfg.bits, slots,
+                                                            npg, cfg.page_size, method="gemm")
+        P = cfg.page_size
+        for kv, x in enumerate((xk, xv)):
+            rows = got_cache[slots // P, h, kv, slots % P, :]
+            codes = oracle.slots_to_groups(oracle.unpack_rows(rows, cfg.bits, cfg.n_groups)).reshape(-1)
+            z = oracle.coupled_vectors(x[:, :, 0, :], cfg.Tc, cfg.c, 0).reshape(-1, cfg.G)
+            assert oracle.accepts(z, cb[0, h, kv].astype(np.float64), results[(0, 0, kv)], codes).all()
+        o_ref, lse_ref = oracle.decode_attention(np.asarray(q[b], np.float64)[h * grp:(h + 1) * grp], ref_cache[0],
+                                                 bt[b], n, cb[0, h:h + 1], t, cfg.Tc, cfg.c, cfg.bits, cfg.base)
+        err = np.abs(o[b, h * grp:(h + 1) * grp] - o_ref)
+        ratio = float((err / bound(o_ref, cfg.io_dtype)).max())
+        _note(f"GPU-coded 32K cache, request {b} head {h}: near-ties {ties}, max err {err.max():.2e} "
+              f"(bound ratio {ratio:.2f})")
+        assert ratio <= 1.0
+        assert np.allclose(lse[b, h * grp:(h + 1) * grp], lse_ref, rtol=0, atol=1e-4)
 
 
 def test_full_size_decode_16_token_pages():
