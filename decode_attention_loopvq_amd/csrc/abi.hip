@@ -51,7 +51,7 @@ int check_dims(const loopvq_dims* d) {
 int n_codebook_groups(const loopvq_dims* d) { return d->per_group ? d->D / d->c : 1; }
 
 struct DecodePlan {
-  int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid, shared_rope;
+  int grp, n_pairs, NT, n_dg, Lc, n_chunks, items_per_head, wg_per_head, grid, shared_rope, quad;
   size_t n_part, bytes_o, bytes_lse;
   size_t bytes_wo, bytes_wl;   // bf16-token partials: one per (KV head, pair)
   size_t total() const { return bytes_o + bytes_lse + bytes_wo + bytes_wl; }
@@ -65,15 +65,24 @@ DecodePlan plan_decode(const loopvq_dims* d, int B, int max_seq_len) {
   pl.grp = d->H_q / d->H_kv;
   pl.n_pairs = B * pl.grp;
   pl.NT = 16;
-  pl.n_dg = std::max(1, (pl.n_pairs + 1) / 2);
+  // quads (four query heads of one request per wave) when the GQA group is a
+  // multiple of four, with bf16 queries, pages of 16 or more positions and one
+  // codebook per (block, head, K|V); else duos of two pairs
+  pl.quad = pl.grp % 4 == 0 && d->io_dtype == LOOPVQ_DTYPE_BF16 && d->page_size >= 16 && !d->per_group;
+  pl.n_dg = std::max(1, (pl.n_pairs + (pl.quad ? 3 : 1)) / (pl.quad ? 4 : 2));
   const long long len = std::max(max_seq_len, 1);
   // workgroup-shared RoPE rows: the eight waves of a workgroup must hold eight
   // duos of one chunk (pages of >= 16 positions, bf16 queries)
   pl.shared_rope = pl.n_dg % 8 == 0 && d->page_size >= 16 && d->io_dtype == LOOPVQ_DTYPE_BF16;
   const long long work = (long long)d->H_kv * pl.n_dg * len;
   const long long step2 = (pl.shared_rope ? 4LL : 2LL) * pl.NT;   // steps per loop iteration
-  // about 2048 waves (8 per CU) over the whole call
-  long long Lc = (work + 2047) / 2048;
+  // about 2048 waves (8 per CU) over the whole call.  Quads about 16384, in
+  // chunks of at least 512 positions: their workgroups take (group, chunk)
+  // items in order of decreasing work, so on ragged batches the many short
+  // items of the later rounds even out the CUs' loads
+  const long long waves = pl.quad ? 16384 : 2048;
+  long long Lc = (work + waves - 1) / waves;
+  if (pl.quad) Lc = std::max(Lc, 512LL);
   Lc = (Lc + step2 - 1) / step2 * step2;
   // shared rows keep each chunk's page ids in a DECODE_PAGE_LIST-entry list
   // per stream.  Chunks start at multiples of Lc, a multiple of step2: when
@@ -414,6 +423,7 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
   p.log2P = ilog2(dims->page_size);
   p.n_pairs = pl.n_pairs;
   p.n_dg = pl.n_dg;
+  p.quad = pl.quad;
   p.shared_rope = pl.shared_rope;
   p.Lc = pl.Lc;
   p.n_chunks = pl.n_chunks;
@@ -423,15 +433,25 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)dims->D);
   p.scale_log2 = scale * 1.4426950408889634f;
   const bool qf32 = dims->io_dtype == LOOPVQ_DTYPE_F32;
+  int grid = pl.grid;
+  if (tasq != nullptr && pl.quad) {
+    // the TaSQ kernel serves duos: the plan's chunks (and so the workspace)
+    // stay, with two waves per quad's pairs
+    p.quad = 0;
+    p.n_dg = std::max(1, (pl.n_pairs + 1) / 2);
+    p.items_per_head = p.n_dg * pl.n_chunks;
+    p.wg_per_head = (p.items_per_head + 7) / 8;
+    grid = dims->H_kv * p.wg_per_head;
+  }
   if (tasq != nullptr) {
     // step t's weights, its block's permutations and its sigma array
     p.tq_w = tasq->w + (size_t)(t - 1) * dims->H_kv * dims->D;
     p.tq_perm = tasq->perm + (size_t)((t - 1) / dims->Tc) * dims->H_kv * (dims->D / 2);
     p.tq_sigma = tasq->sigma + (size_t)(t - 1) * tasq->sigma_stride;
-    return hip_status(launch_decode_split_tq(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
+    return hip_status(launch_decode_split_tq(dims->D, dims->c, dims->bits, qf32, p, grid, stream));
   }
-  if (dims->per_group) return hip_status(launch_decode_split_pg(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
-  return hip_status(launch_decode_split(dims->D, dims->c, dims->bits, qf32, p, pl.grid, stream));
+  if (dims->per_group) return hip_status(launch_decode_split_pg(dims->D, dims->c, dims->bits, qf32, p, grid, stream));
+  return hip_status(launch_decode_split(dims->D, dims->c, dims->bits, qf32, p, grid, stream));
 }
 
 // the combine pass; win_o / win_lse: the bf16-token partials, or null

@@ -19,7 +19,11 @@
 //  * A wave serves a duo of (request, query head) pairs 2i and 2i+1 over a
 //    chunk of positions, 16 positions per step.  When the GQA group is even
 //    the duo's pairs are query heads of one request and share one index
-//    stream and its key gathers.
+//    stream and its key gathers.  With a GQA group that is a multiple of
+//    four (G4) a wave serves a quad, pairs 4i .. 4i+3, all query heads of one
+//    request and KV head: one index stream, one set of key gathers, two K
+//    MFMAs per frequency (pairs 0-1 and 2-3) on the same key column, and
+//    each V lane accumulates two query heads from one set of value gathers.
 //  * K side: a lane owns one position (of its 16-lane row) and one quarter
 //    of the RoPE frequencies.  For each frequency one v_mfma_f32_4x4x4f16 with
 //    the block-diagonal query matrix [[q0_f, q0_h], [q0_h, -q0_f]] (+) the same
@@ -113,8 +117,9 @@ __device__ __forceinline__ Entry<EB> lds_entry(const uint8_t* lds, uint32_t addr
   return e;
 }
 
-template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP, bool ST, bool PG, bool TQ>
+template <int D, int C, int BITS, bool QF32, bool SHARE, bool SP, bool ST, bool PG, bool TQ, bool G4>
 __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
+  static_assert(!G4 || (SHARE && SP && !QF32 && !PG && !TQ), "quads: one request per wave, bf16 queries, pages of 16+");
   constexpr int N = D / C;            // groups per row
   constexpr int Q = N / 8;            // lo (and hi) groups per lane quarter
   constexpr int F = D / 8;            // RoPE frequencies per lane quarter (one K MFMA each)
@@ -128,7 +133,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   constexpr int KENT = 1 << BITS;
   constexpr int NS = SHARE ? 1 : 2;   // index streams per wave: the duo's requests
   constexpr int NT = 16;              // positions per wave step
-  constexpr int SW = 4 * U + 3;       // floats of one lane's softmax state (one pair)
+  constexpr int PW = G4 ? 4 : 2;      // (request, query head) pairs per wave
+  constexpr int HPL = G4 ? 2 : 1;     // query heads per V lane
   constexpr int WAVES = 8;            // waves per workgroup, all on one KV head
   constexpr int TSTEP = NT * D * 4;   // bytes of the RoPE rows of one step
   // slices: shared codebook, every entry replicated over a 256-byte row;
@@ -137,21 +143,118 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   constexpr int LDS_RING = ST ? 2 * TSTEP : 0;
   constexpr int PGMAX = DECODE_PAGE_LIST;   // page-list entries per stream and wave (shared rows)
   constexpr int LDS_PAGES = ST ? WAVES * 2 * PGMAX * 4 : 0;
-  constexpr int LDS_MERGE = WAVES * 64 * SW * 4;
-  constexpr int LDS_BYTES = LDS_SLICES + LDS_RING + LDS_PAGES > LDS_MERGE ? LDS_SLICES + LDS_RING + LDS_PAGES
-                                                                          : LDS_MERGE;
+  constexpr int LDS_BYTES = LDS_SLICES + LDS_RING + LDS_PAGES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int wsteps[WAVES];
   __shared__ int tqinv[TQ ? D / 2 : 1];     // TaSQ: u pair of each RoPE frequency
+  // G4: requests in order of decreasing coded length (ties by index), so that
+  // the eight quads of a workgroup, which it runs in step, have similar lengths
+  __shared__ int req_sorted[G4 ? DECODE_SORT_MAX : 1];
+  __shared__ __attribute__((aligned(16))) int len_sorted[G4 ? DECODE_SORT_MAX : 1];
+  __shared__ int wg_busy;
+  __shared__ int wg_item[2];                // G4 with shared rows: (group of 8 quads, chunk)
 
   // ---- workgroup -> (KV head, 8 work items).  Heads vary fastest, so each
   //      XCD (blocks of one residue mod 8, renumbered contiguously) owns a
   //      band of chunks of every head: its L2 holds only that band's RoPE rows.
+  //      Quads (ragged GQA batches, whose chunks and requests differ in work)
+  //      keep the hardware's interleaving instead: every XCD then gets an
+  //      equal share of long and short work items, and the workgroups, which
+  //      come in order of decreasing work, are handed out as CUs free up.
   int bid = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if (!G4 && (nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int wgi = bid / p.H_kv;
   const int h = bid - wgi * p.H_kv;
+
+  // ---- G4: rank the requests by length (every workgroup computes the same
+  //      order from seq_lens), then leave at once if none of this workgroup's
+  //      quads has positions in its chunk (nothing staged, nothing written)
+  const bool sorted = G4 && p.B <= DECODE_SORT_MAX;
+  if constexpr (G4) {
+    if (sorted) {
+      // lengths padded with -1 to a multiple of 4 (padding ranks after every request)
+      const int B4 = (p.B + 3) & ~3;
+      for (int t = threadIdx.x; t < B4; t += WAVES * 64)
+        len_sorted[t] = t < p.B ? min(max(p.seq_lens[t], 0), p.max_seq_len) : -1;
+      __syncthreads();
+      for (int t = threadIdx.x; t < p.B; t += WAVES * 64) {
+        const int lt = len_sorted[t];
+        int r = 0;
+        for (int j = 0; j < B4; j += 4) {
+          const int4 lj = *(const int4*)(len_sorted + j);
+          r += (lj.x > lt || (lj.x == lt && j < t)) ? 1 : 0;
+          r += (lj.y > lt || (lj.y == lt && j + 1 < t)) ? 1 : 0;
+          r += (lj.z > lt || (lj.z == lt && j + 2 < t)) ? 1 : 0;
+          r += (lj.w > lt || (lj.w == lt && j + 3 < t)) ? 1 : 0;
+        }
+        req_sorted[r] = t;
+      }
+    }
+    // with shared rows (eight quads per workgroup, one chunk) the workgroups
+    // take the (group of 8 quads, chunk) items in order of decreasing work:
+    // a group is 8 quads in length order, its work in chunk c is
+    // clamp(L - c*Lc, 0, Lc) positions (L its longest request).  Full chunks
+    // come first (group-major), then each group's last, partial chunk by
+    // decreasing size; the hardware starts workgroups in index order, so each
+    // round of workgroups holds items of similar size
+    if (threadIdx.x == 0) {
+      wg_busy = 0;
+      wg_item[0] = -1;
+      wg_item[1] = 0;
+    }
+    __syncthreads();
+    const int n_groups = p.n_dg / WAVES;
+    if (ST && sorted && n_groups <= 64) {
+      if (threadIdx.x < 64) {
+        const int g = (int)threadIdx.x;
+        const int qpr = p.grp >> 2;
+        const int Lg = g < n_groups ? len_sorted[req_sorted[(WAVES * g) / qpr]] : 0;
+        const int fc = Lg / p.Lc, pr = Lg - fc * p.Lc;
+        // inclusive prefix of the full-chunk counts over the groups
+        int inc = fc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int o = __shfl_up(inc, d);
+          if (g >= d) inc += o;
+        }
+        const int F = __shfl(inc, 63);
+        const int it = wgi;
+        if (it < F) {
+          if (it >= inc - fc && it < inc) {
+            wg_item[0] = g;
+            wg_item[1] = it - (inc - fc);
+          }
+        } else {
+          // partial chunks: rank by (size desc, group asc)
+          int rank = 0;
+#pragma unroll
+          for (int o = 0; o < 64; ++o) {
+            const int po = __builtin_amdgcn_readlane(pr, o);
+            rank += (po > pr || (po == pr && o < g)) ? 1 : 0;
+          }
+          if (pr > 0 && rank == it - F) {
+            wg_item[0] = g;
+            wg_item[1] = fc;
+          }
+        }
+      }
+      __syncthreads();
+      if (wg_item[0] < 0) return;   // workgroup-uniform: no work left for this item number
+    } else {
+      if (threadIdx.x < WAVES) {
+        const int it = wgi * WAVES + (int)threadIdx.x;
+        if (it < p.items_per_head) {
+          const int c0 = it / p.n_dg, qd = it - c0 * p.n_dg;
+          const int bs = qd / (p.grp >> 2);
+          const int b = sorted ? req_sorted[bs] : bs;
+          if (c0 * p.Lc < min(max(p.seq_lens[b], 0), p.max_seq_len)) atomicOr(&wg_busy, 1);
+        }
+      }
+      __syncthreads();
+      if (wg_busy == 0) return;   // workgroup-uniform
+    }
+  }
 
   // ---- stage the K and V slices of head h, each entry replicated over a
   //      256-byte row (one copy per bank window): entry e of region kv sits
@@ -210,7 +313,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // ---- this wave's work item (wave-uniform): one duo of pairs, one chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int item = wgi * WAVES + wave;
+  // G4 with shared rows and ordered items: group wg_item[0], chunk wg_item[1]
+  const bool ordered = G4 && ST && sorted && p.n_dg / WAVES <= 64;
+  const int item = ordered ? (wg_item[1] * p.n_dg + wg_item[0] * WAVES + wave) : wgi * WAVES + wave;
   const bool item_ok = item < p.items_per_head;
   const int ch = item_ok ? item / p.n_dg : 0;
   const int duo = item_ok ? item - ch * p.n_dg : 0;
@@ -221,29 +326,45 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // a bf16 sink attended elsewhere); has[s]: the stream has coded positions
   int kq[2], bq[2], len[2], lo[2];
   bool okq[2], has[2];
+  // G4: the quad's first pair (its request taken in length order)
+  int pair0 = PW * duo;
+  if constexpr (G4) {
+    const int qpr = p.grp >> 2;                  // quads per request
+    const int bs = duo / qpr;
+    pair0 = (sorted ? req_sorted[min(bs, p.B - 1)] : bs) * p.grp + (duo - bs * qpr) * 4;
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    kq[s] = 2 * duo + s;
+    kq[s] = pair0 + s;
     okq[s] = item_ok && kq[s] < p.n_pairs;
     bq[s] = okq[s] ? kq[s] / p.grp : 0;
     len[s] = okq[s] ? min(max(p.seq_lens[bq[s]], 0), p.max_seq_len) : 0;
     lo[s] = (okq[s] && p.seq_lo != nullptr) ? min(max(p.seq_lo[bq[s]], 0), len[s]) : 0;
     has[s] = lo[s] < len[s];
   }
+  // G4: pairs 2 and 3 of the quad (the same request as pairs 0 and 1)
+  bool okq_hi[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) okq_hi[s] = G4 && item_ok && pair0 + 2 + s < p.n_pairs;
   const int p0 = ch * p.Lc;
   const int lenx = max(len[0], len[1]);
   const bool active = item_ok && p0 < lenx;   // wave-uniform
 
-  // V role: rows 0-1 of the wave serve pair 0 and rows 2-3 pair 1; a lane
-  // takes the adjacent positions 8*rp + 2*la and 8*rp + 2*la + 1 of the step
-  // and channel quarter lb
+  // V role: rows 0-1 of the wave serve pair 0 and rows 2-3 pair 1 (G4: pairs
+  // 0, 1 and pairs 2, 3); a lane takes the adjacent positions 8*rp + 2*la and
+  // 8*rp + 2*la + 1 of the step and channel quarter lb
   const int sv = row >> 1, rp = row & 1;
-  float m = -INFINITY;                   // running max (log2 domain)
-  float l = 0.f;                         // sum of the rounded p used in the products
-  float lx = 0.f;                        // exact sum of p (for the logsumexp)
-  float4v acc[U];
+  float m[HPL], l[HPL], lx[HPL];         // running max (log2 domain); sum of the rounded p
+                                         // used in the products; exact sum of p (logsumexp)
+  float4v acc[HPL][U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < HPL; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+    lx[j] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[j][u] = (float4v){0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- K-side A operands (read by active waves only).  For frequency f (the
   //      i-th of quarter la) lane lb supplies row lb of the block-diagonal
@@ -257,6 +378,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      (k_f, k_h, k_f, k_h) of one stream, so one product covers both pairs
   //      when they share keys and two (one per stream) when they do not.
   half4v AK[F];
+  half4v AK2[G4 ? F : 1];                // G4: the same rows for pairs 2 and 3
   // TaSQ: u pair of the lane's i-th frequency slot: the pairs of its quarter's
   // lo groups, then those of its hi groups
   auto tq_upair = [&](int i) { return i < F / 2 ? la * (F / 2) + i : D / 4 + la * (F / 2) + (i - F / 2); };
@@ -291,8 +413,18 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
     const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
     const size_t qoff = ((size_t)bb * p.H_q + jq) * D + la * F;
+    // G4: query head of pair 2 + s (clamped to a valid head of the request)
+    const int jq2 = h * p.grp + (okq_hi[s] ? kk + 2 - bb * p.grp : 0);
+    const size_t qoff2 = ((size_t)bb * p.H_q + jq2) * D + la * F;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
+      if constexpr (G4) {
+        const float a2 = u2f((uint32_t)((const uint16_t*)p.q)[qoff2 + i] << 16);
+        const float c2 = u2f((uint32_t)((const uint16_t*)p.q)[qoff2 + D / 2 + i] << 16);
+        const _Float16 g0 = (_Float16)((lb & 1) ? c2 : a2), g1 = (_Float16)((lb & 1) ? -a2 : c2);
+        const _Float16 zz = (_Float16)0.f;
+        AK2[i] = s ? (half4v){zz, zz, g0, g1} : (half4v){g0, g1, zz, zz};
+      }
       float a, c;
       if constexpr (QF32) {
         a = ((const float*)p.q)[qoff + i];
@@ -323,6 +455,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   // score after the quarter sum
   const int bperm_a = ((16 * (2 * rp + (la >> 1))) | ((2 * sv + (lb & 1)) << 2) | (2 * (la & 1))) << 2;
   const int bperm_b = bperm_a + 4;
+  // G4: K-role lane of quarter la exposes pair la; my heads 2*sv + j at my
+  // two positions sit at quarter 2*sv + j, slots 2*(la%2) (+1)
+  const int bperm_g4 = ((16 * (2 * rp + (la >> 1))) | ((2 * sv) << 2) | (2 * (la & 1))) << 2;
   const int P = 1 << p.log2P;
   const uint32_t kv_stride = (uint32_t)(P * R);             // V rows follow the K rows of a page
   // bytes between pages (below 2^32: the boundary rejects larger strides), so
@@ -498,6 +633,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      lane's quarter; klo/khi and tb hold the step's entries and rows)
   auto k_side = [&](float* sc) {
     float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
+    float sa2 = 0.f, sb2 = 0.f, sa3 = 0.f, sb3 = 0.f;   // G4: pairs 2 and 3
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < F; ++i) {
@@ -534,6 +670,17 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
           }
         } else {
           xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w0, w1}), zero, 0, 0, 0);
+          if constexpr (G4) {
+            // pairs 2 and 3 on the same key column
+            const float4v xy2 =
+                __builtin_amdgcn_mfma_f32_4x4x4f16(AK2[i], __builtin_bit_cast(half4v, (uint2v){w0, w0}), zero, 0, 0, 0);
+            const float cs2 = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
+            const float sn2 = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
+            sa2 = fmaf(cs2, xy2.x, sa2);
+            sb2 = fmaf(sn2, xy2.y, sb2);
+            sa3 = fmaf(cs2, xy2.z, sa3);
+            sb3 = fmaf(sn2, xy2.w, sb3);
+          }
         }
       }
       const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
@@ -545,8 +692,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     // interleave: each MFMA is followed by VALU work (the next perms and this
     // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
-    constexpr int KMF = (TQ || QF32) ? (SHARE ? 1 : 2) : 1;
-    constexpr int KVALU = TQ ? 4 : 6;
+    constexpr int KMF = (TQ || QF32) ? (SHARE ? 1 : 2) : (G4 ? 2 : 1);
+    constexpr int KVALU = TQ ? 4 : (G4 ? 9 : 6);
 #pragma unroll
     for (int i = 0; i < F; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, KMF, 0);
@@ -554,11 +701,30 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     sc[0] = sa0 + sb0;
     sc[1] = sa1 + sb1;
+    if constexpr (G4) {
+      sc[2] = sa2 + sb2;
+      sc[3] = sa3 + sb3;
+    }
   };
   // sum over the four quarters (lanes 4 apart within the 16-lane row); lanes
   // of quarters 0-1 then expose pair 0's score and quarters 2-3 pair 1's, and
   // each V lane pulls its two positions of its pair
   auto to_v_role = [&](const float* sc, float* sv2) {
+    if constexpr (G4) {
+      // quarter la exposes pair la; the V lane pulls pairs 2*sv, 2*sv + 1 at
+      // its two positions: sv2[2*j + e] = score of head j at position e
+      float v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[k] = sc[k];
+        v[k] += u2f(__builtin_amdgcn_mov_dpp(f2u(v[k]), 0x124, 0xf, 0xf, true));   // row_ror:4
+        v[k] += u2f(__builtin_amdgcn_mov_dpp(f2u(v[k]), 0x128, 0xf, 0xf, true));   // row_ror:8
+      }
+      const uint32_t ex = f2u(la == 0 ? v[0] : (la == 1 ? v[1] : (la == 2 ? v[2] : v[3])));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sv2[k] = u2f(__builtin_amdgcn_ds_bpermute(bperm_g4 + 16 * (k >> 1) + 4 * (k & 1), ex));
+      return;
+    }
     float v0 = sc[0], v1 = sc[1];
     v0 += u2f(__builtin_amdgcn_mov_dpp(f2u(v0), 0x124, 0xf, 0xf, true));   // row_ror:4
     v1 += u2f(__builtin_amdgcn_mov_dpp(f2u(v1), 0x124, 0xf, 0xf, true));
@@ -575,66 +741,70 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   auto v_side = [&](int g0, const float* sv2, uint32_t sg) {
     const int posa = g0 + vrel;
     const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 1) < vspan;
-    float s0 = sv2[0], s1 = sv2[1];
-    if constexpr (TQ) {
-      // the rebuilt key is sigma * P^-1(u_hat) / w: the score scales by sigma
-      s0 *= (float)as_h2(sg).x;
-      s1 *= (float)as_h2(sg).y;
-    }
-    const float sa = va ? s0 * p.scale_log2 : -INFINITY;
-    const float sb = vb ? s1 * p.scale_log2 : -INFINITY;
-    const float smax = fmaxf(sa, sb);
-    const bool need = smax > m + LAZY_TAU;
-    if (__ballot(need) != 0) {
-      if (need) {
-        const float fct = __builtin_amdgcn_exp2f(m - smax);
-        l *= fct;
-        lx *= fct;
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] *= fct;
-        m = smax;
+    for (int j = 0; j < HPL; ++j) {      // G4: the lane's two query heads share the V gathers
+      float s0 = sv2[2 * j], s1 = sv2[2 * j + 1];
+      if constexpr (TQ) {
+        // the rebuilt key is sigma * P^-1(u_hat) / w: the score scales by sigma
+        s0 *= (float)as_h2(sg).x;
+        s1 *= (float)as_h2(sg).y;
       }
-    }
-    const float pa = va ? __builtin_amdgcn_exp2f(sa - m) : 0.f;
-    const float pb = vb ? __builtin_amdgcn_exp2f(sb - m) : 0.f;
-    lx += pa + pb;
-    half4v A[2], Alo[2];
-    const float pv[2] = {pa, pb};
+      const float sa = va ? s0 * p.scale_log2 : -INFINITY;
+      const float sb = vb ? s1 * p.scale_log2 : -INFINITY;
+      const float smax = fmaxf(sa, sb);
+      const bool need = smax > m[j] + LAZY_TAU;
+      if (__ballot(need) != 0) {
+        if (need) {
+          const float fct = __builtin_amdgcn_exp2f(m[j] - smax);
+          l[j] *= fct;
+          lx[j] *= fct;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const _Float16 ph = (_Float16)pv[t];
-      const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
-      A[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
-      // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
-      if constexpr (QF32) {
-        const _Float16 pl = (_Float16)(pv[t] - (float)ph);
-        const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
-        Alo[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
-        l += (float)ph + (float)pl;
-      } else {
-        l += (float)ph;
+          for (int u = 0; u < U; ++u) acc[j][u] *= fct;
+          m[j] = smax;
+        }
       }
-    }
+      const float pa = va ? __builtin_amdgcn_exp2f(sa - m[j]) : 0.f;
+      const float pb = vb ? __builtin_amdgcn_exp2f(sb - m[j]) : 0.f;
+      lx[j] += pa + pb;
+      half4v A[2], Alo[2];
+      const float pv[2] = {pa, pb};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
+        const _Float16 ph = (_Float16)pv[t];
+        const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
+        A[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
+        // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
+        if constexpr (QF32) {
+          const _Float16 pl = (_Float16)(pv[t] - (float)ph);
+          const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
+          Alo[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
+          l[j] += (float)ph + (float)pl;
+        } else {
+          l[j] += (float)ph;
+        }
+      }
+      float4v* ac = acc[j];
 #pragma unroll
-      for (int sl = 0; sl < 2 * Q; ++sl) {
-        if constexpr (EB == 8) {
-          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
-          acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, acc[sl], 0, 0, 0);
-          if constexpr (QF32) acc[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, acc[sl], 0, 0, 0);
-        } else if constexpr (EB == 16) {
-          const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
-          const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[2], ve[t][sl].d[3]});
-          acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B0, acc[2 * sl], 0, 0, 0);
-          if constexpr (QF32) acc[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B0, acc[2 * sl], 0, 0, 0);
-          acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B1, acc[2 * sl + 1], 0, 0, 0);
-          if constexpr (QF32) acc[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B1, acc[2 * sl + 1], 0, 0, 0);
-        } else if (sl & 1) {
-          // two 2-channel entries form one 4-channel unit
-          const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl - 1].d[0], ve[t][sl].d[0]});
-          acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, acc[sl >> 1], 0, 0, 0);
-          if constexpr (QF32) acc[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, acc[sl >> 1], 0, 0, 0);
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int sl = 0; sl < 2 * Q; ++sl) {
+          if constexpr (EB == 8) {
+            const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
+            ac[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, ac[sl], 0, 0, 0);
+            if constexpr (QF32) ac[sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, ac[sl], 0, 0, 0);
+          } else if constexpr (EB == 16) {
+            const half4v B0 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
+            const half4v B1 = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[2], ve[t][sl].d[3]});
+            ac[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B0, ac[2 * sl], 0, 0, 0);
+            if constexpr (QF32) ac[2 * sl] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B0, ac[2 * sl], 0, 0, 0);
+            ac[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], B1, ac[2 * sl + 1], 0, 0, 0);
+            if constexpr (QF32) ac[2 * sl + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], B1, ac[2 * sl + 1], 0, 0, 0);
+          } else if (sl & 1) {
+            // two 2-channel entries form one 4-channel unit
+            const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl - 1].d[0], ve[t][sl].d[0]});
+            ac[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[t], Bv, ac[sl >> 1], 0, 0, 0);
+            if constexpr (QF32) ac[sl >> 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Alo[t], Bv, ac[sl >> 1], 0, 0, 0);
+          }
         }
       }
     }
@@ -653,7 +823,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       // when the step's V entries are gathered, before the rows are refilled)
       uint32_t sgc = 0u;
       auto do_step = [&](int st, uint32_t (*kwn)[LW], uint32_t (*vwn)[LW], uint32_t& sgn, int* pgr) {
-        float sc[2], sv2[2];
+        float sc[PW], sv2[2 * HPL];
         k_side(sc);
         table_load(st + 1);                             // RoPE rows of step st+1
         to_v_role(sc, sv2);
@@ -787,7 +957,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       page_lds(st + 4, pgn);
       __builtin_amdgcn_sched_barrier(0);
       if (st < my_steps) {
-        float sc[2], sv2[2];
+        float sc[PW], sv2[2 * HPL];
         table_lds(st);
         k_side(sc);
         __builtin_amdgcn_sched_barrier(0);
@@ -826,55 +996,59 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   }
 
   // ---- merge the 8 position slots of each (pair, quarter) and write the
-  //      chunk's partials
-  __syncthreads();                       // every wave is done with the slices
-  float* red = (float*)lds + (size_t)wave * 64 * SW;
-  {
-    float* r = red + lane * SW;
+  //      chunk's partials.  The slots of one (pair, quarter) are the lanes of
+  //      rows 2*sv, 2*sv + 1 at slots la = 0..3 of one quarter lb: 4 and 8
+  //      lanes apart inside a row and 16 apart across the two rows.  Three
+  //      exchange rounds (DPP row rotations by 4 and 8, then a swizzle that
+  //      swaps the two rows) leave the merged state in each of the 8 lanes;
+  //      every wave merges its own lanes, so no barrier or LDS is involved.
+  auto xchg = [&](float v, int round) -> float {
+    if (round == 0) return u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x124, 0xf, 0xf, true));   // row_ror:4
+    if (round == 1) return u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x128, 0xf, 0xf, true));   // row_ror:8
+    return u2f(__builtin_amdgcn_ds_swizzle(f2u(v), 0x401f));                                // lane ^ 16
+  };
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      r[4 * u] = acc[u].x; r[4 * u + 1] = acc[u].y; r[4 * u + 2] = acc[u].z; r[4 * u + 3] = acc[u].w;
-    }
-    r[4 * U] = m;
-    r[4 * U + 1] = l;
-    r[4 * U + 2] = lx;
-  }
-  __syncthreads();
-  // one lane per (pair, quarter): row 2*sv, position slot la == 0
-  if (active && okq[sv] && rp == 0 && la == 0 && p0 < len[sv]) {
-    float M = -INFINITY;
-    for (int i = 0; i < 8; ++i) {
-      const float* r = red + ((2 * sv + (i >> 2)) * 16 + (i & 3) * 4 + lb) * SW;
-      if (r[4 * U + 1] > 0.f) M = fmaxf(M, r[4 * U]);
-    }
-    float4v o[U];
+  for (int round = 0; round < 3; ++round) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) o[u] = (float4v){0.f, 0.f, 0.f, 0.f};
-    float L = 0.f, LX = 0.f;
-    for (int i = 0; i < 8; ++i) {
-      const float* r = red + ((2 * sv + (i >> 2)) * 16 + (i & 3) * 4 + lb) * SW;
-      if (!(r[4 * U + 1] > 0.f)) continue;
-      const float wt = __builtin_amdgcn_exp2f(r[4 * U] - M);
+    for (int j = 0; j < HPL; ++j) {
+      const float mo = xchg(m[j], round), lo2 = xchg(l[j], round), lxo = xchg(lx[j], round);
+      // an empty state (no positions yet: l = 0, m = -inf) carries weight 0
+      const float M = fmaxf(m[j], mo);
+      const float w1 = l[j] > 0.f ? __builtin_amdgcn_exp2f(m[j] - M) : 0.f;
+      const float w2 = lo2 > 0.f ? __builtin_amdgcn_exp2f(mo - M) : 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        o[u].x = fmaf(wt, r[4 * u], o[u].x);
-        o[u].y = fmaf(wt, r[4 * u + 1], o[u].y);
-        o[u].z = fmaf(wt, r[4 * u + 2], o[u].z);
-        o[u].w = fmaf(wt, r[4 * u + 3], o[u].w);
+        float4v a = acc[j][u];
+        a.x = fmaf(w2, xchg(a.x, round), w1 * a.x);
+        a.y = fmaf(w2, xchg(a.y, round), w1 * a.y);
+        a.z = fmaf(w2, xchg(a.z, round), w1 * a.z);
+        a.w = fmaf(w2, xchg(a.w, round), w1 * a.w);
+        acc[j][u] = a;
       }
-      L = fmaf(wt, r[4 * U + 1], L);
-      LX = fmaf(wt, r[4 * U + 2], LX);
+      l[j] = fmaf(w2, lo2, w1 * l[j]);
+      lx[j] = fmaf(w2, lxo, w1 * lx[j]);
+      m[j] = l[j] > 0.f ? M : -INFINITY;
     }
-    const size_t part = (size_t)(h * p.n_pairs + kq[sv]) * p.n_chunks + ch;
+  }
+  // one lane per (pair, quarter) writes: row 2*sv, position slot la == 0
+  // (G4: for each of its two query heads, pairs 2*sv and 2*sv + 1 of the quad)
+#pragma unroll
+  for (int j = 0; j < HPL; ++j) {
+    const int pj = G4 ? 2 * sv + j : sv;                   // pair of the wave
+    const bool okj = G4 ? (pj < 2 ? okq[pj] : okq_hi[pj - 2]) : okq[sv];
+    if (!(active && okj && rp == 0 && la == 0 && p0 < len[G4 ? 0 : sv])) continue;
+    const int kpair = G4 ? pair0 + pj : kq[sv];
+    const size_t part = (size_t)(h * p.n_pairs + kpair) * p.n_chunks + ch;
+    const float L = l[j];
     const float inv = L > 0.f ? 1.f / L : 0.f;
     float* op = p.part_o + part * D;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int lc = 4 * u;
       const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
-      *(float4v*)(op + base) = o[u] * inv;
+      *(float4v*)(op + base) = acc[j][u] * inv;
     }
-    if (lb == 0) p.part_lse[part] = L > 0.f ? M + log2f(LX) : -INFINITY;
+    if (lb == 0) p.part_lse[part] = L > 0.f ? m[j] + log2f(lx[j]) : -INFINITY;
   }
 }
 
@@ -884,25 +1058,40 @@ static void launch_split_sp(const DecodeParams& p, int grid, hipStream_t s) {
   // a step's 16 positions lie in one page when pages hold at least 16
   // positions; workgroup-shared RoPE rows need eight duos per head
   if (p.log2P < 4) {
-    hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false, false, PG, TQ>), dim3(grid), dim3(512), 0,
-                       s, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, false, false, PG, TQ, false>), dim3(grid),
+                       dim3(512), 0, s, p);
     return;
   }
   if constexpr (!QF32) {
     if (p.shared_rope) {
-      hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, SHARE, true, true, PG, TQ>), dim3(grid), dim3(512), 0,
-                         s, p);
+      hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, SHARE, true, true, PG, TQ, false>), dim3(grid),
+                         dim3(512), 0, s, p);
       return;
     }
   }
-  hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true, false, PG, TQ>), dim3(grid), dim3(512), 0, s,
-                     p);
+  hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, QF32, SHARE, true, false, PG, TQ, false>), dim3(grid),
+                     dim3(512), 0, s, p);
 }
 
 template <int D, int C, int BITS, bool PG, bool TQ>
 static hipError_t launch_split_t(const DecodeParams& p, bool qf32, int grid, hipStream_t s) {
   // pairs 2i and 2i+1 belong to one request when the GQA group size is even
   const bool share = (p.grp & 1) == 0;
+  if constexpr (!PG && !TQ) {
+    // quads: four query heads of one request per wave (the split plan sets
+    // this for bf16 queries, pages of 16 or more and a group of 4, 8, ...)
+    if (p.quad) {
+      if (qf32 || p.log2P < 4 || (p.grp & 3) != 0) return hipErrorInvalidValue;
+      if (p.shared_rope)
+        hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, true, true, true, false, false, true>), dim3(grid),
+                           dim3(512), 0, s, p);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<D, C, BITS, false, true, true, false, false, false, true>), dim3(grid),
+                           dim3(512), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.quad) return hipErrorInvalidValue;
   if (qf32) {
     if (share) launch_split_sp<D, C, BITS, true, true, PG, TQ>(p, grid, s);
     else launch_split_sp<D, C, BITS, true, false, PG, TQ>(p, grid, s);

@@ -10,6 +10,9 @@ namespace loopvq {
 // entries of the per-wave page lists of the workgroup-shared RoPE path (per
 // stream): a chunk of the split plan must span at most this many pages
 constexpr int DECODE_PAGE_LIST = 128;
+// batches of up to this many requests are taken in length order by the quad
+// decode (larger ones in index order)
+constexpr int DECODE_SORT_MAX = 512;
 
 struct DecodeParams {
   const void* q;              // [B][H_q][D] bf16 or fp32
@@ -28,9 +31,10 @@ struct DecodeParams {
   float* part_lse;            // [H_kv][n_pairs][n_chunks], log2 domain
   int B, H_kv, H_q, grp, max_pages, log2P;
   int n_pairs;                // B * grp (request, query head) pairs per KV head
-  int n_dg;                   // duos (pairs 2i, 2i+1) per KV head; one wave serves one duo
+  int n_dg;                   // duos (pairs 2i, 2i+1), or quads (4i .. 4i+3), per KV head; one per wave
   int Lc;                     // positions per chunk (one wave), a multiple of 32 (64 if shared_rope)
   int shared_rope;            // eight waves of a workgroup share a chunk and its RoPE rows
+  int quad;                   // a wave serves four query heads of one request (else two pairs)
   int n_chunks;
   int items_per_head;         // n_dg * n_chunks wave work items per KV head
   int wg_per_head;            // ceil(items_per_head / 8): eight waves per workgroup
