@@ -5,8 +5,8 @@
 // "Optimizing pre-RoPE vector quantization serving efficiency"]: at loop step t every
 // cached token j of a request contributes its key rebuilt from the step's
 // codebook slice, rotated by RoPE at position j, and its value rebuilt the
-// same way; tokens are cut into splits whose partial softmax outputs are
-// merged by their logsumexp (the combine kernel), which recovers the exact
+// same way; tokens are cut into splits, and joining the splits' partial
+// softmax outputs by log-sum-exp (the combine kernel) yields exactly the
 // softmax over all tokens.
 //
 // MI355X mapping (this file's own design, not the pages'):

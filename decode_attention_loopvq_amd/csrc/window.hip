@@ -2,11 +2,11 @@
 // and the recent window.
 //
 // What it computes [LoopVQ paper, hub.valency.io/works/W_7srt5hed_v1,
-// section "System implementation", cache layout and attention]: the first
-// n_s tokens and the most recent tokens of a request are kept in bf16 pages
-// of 8 tokens, the rest as codes; at each loop step one kernel attends to the
-// bf16 pages and another to the coded pages, and the partial outputs of both
-// are merged by their logsumexp.  This kernel is the bf16 side: it leaves one
+// section "System implementation", cache layout and attention]: a request's
+// leading n_s tokens and its latest tokens live unquantised in bf16 pages of
+// 8 tokens and every other token as codes; each loop step attends the two
+// kinds of page in separate kernels and joins their partial outputs by
+// log-sum-exp.  This kernel is the bf16 side: it leaves one
 // partial (o, log2-sum-exp) per (request, query head) for the combine kernel.
 // The bf16 pages hold pre-RoPE keys (they are coded later, when the window
 // moves on), so the key is rotated here at its token's position, with the

@@ -212,9 +212,9 @@ size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
 /*
  * Quantised decode attention of B requests at loop step t (1-based).
  * [LoopVQ paper, section "System implementation", attention: at loop step
- * t the kernel looks up each index in B_t, rebuilds K, applies RoPE, and
- * splits the tokens across workgroups whose partial outputs are merged by
- * their logsumexp, which recovers the exact softmax.]
+ * t each index is looked up in B_t to rebuild K, RoPE is applied, and the
+ * tokens are spread over workgroups; joining their partial outputs by
+ * log-sum-exp gives the same softmax as one pass over all tokens.]
  *   t             loop step, 1 <= t <= T; reads block (t-1)/Tc, slice t-1.
  *   q             [B][H_q][D] queries already rotated at their own position.
  *                 bf16 queries enter the matrix cores as fp16 values, so
@@ -333,9 +333,9 @@ typedef struct loopvq_bf16_window {
 /*
  * Decode attention at loop step t over a cache that mixes bf16 pages (sink
  * and recent window) with coded pages.  [LoopVQ paper, section "System
- * implementation", attention: one kernel attends to the bf16 pages and
- * another to the quantised pages, and their split partials are merged by the
- * logsumexp of their scores, which is one softmax over every token.]
+ * implementation", attention: the unquantised pages and the coded pages are
+ * attended by separate kernels, and joining their partials by log-sum-exp
+ * gives a single softmax over every cached token.]
  * Positions [n_sink, win_start) of request b are read as codes through
  * block_table, exactly as loopvq_decode_attn reads positions [0, seq_len);
  * block-table entries of pages that hold no coded position are never read.

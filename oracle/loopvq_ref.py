@@ -310,9 +310,9 @@ def rope_table(max_pos: int, D: int, base: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# attention  [P1 section "System implementation": the split partials are
-#   merged by their logsumexp, which recovers the exact softmax over all
-#   tokens - so the reference is plain dense softmax attention]
+# attention  [P1 section "System implementation": splitting the tokens and
+#   merging the partial results by log-sum-exp changes nothing in the result,
+#   so the reference is plain dense softmax attention over all tokens]
 # --------------------------------------------------------------------------
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
     """o = softmax(sm_scale * k @ q) @ v and lse = log sum exp(sm_scale * k @ q).
@@ -374,11 +374,11 @@ def gather_rows_at(cache: np.ndarray, block_table_row: np.ndarray, pos: np.ndarr
 
 
 # --------------------------------------------------------------------------
-# bf16 sink and recent window  [P1 section "System implementation": the first
-#   n_s tokens and the most recent n_r tokens of a request stay in bf16 and
-#   all others are codes; at loop step t one kernel attends to the bf16 pages
-#   and another to the quantised pages, and the partials of both are merged by
-#   their logsumexp, which is one softmax over every cached token]
+# bf16 sink and recent window  [P1 section "System implementation": a
+#   request keeps its n_s leading tokens and its n_r latest tokens unquantised
+#   (bf16), every other token as codes; the bf16 part and the coded part are
+#   attended separately at loop step t and their partials joined by
+#   log-sum-exp, so the result is a single softmax over all cached tokens]
 # --------------------------------------------------------------------------
 def decode_attention_window(q: np.ndarray, cache_block: np.ndarray, block_table_row: np.ndarray,
                             n: int, n_sink: int, win_start: int, k_bf: np.ndarray, v_bf: np.ndarray,
