@@ -21,9 +21,13 @@
 //    the duo's pairs are query heads of one request and share one index
 //    stream and its key gathers.  With a GQA group that is a multiple of
 //    four (G4) a wave serves a quad, pairs 4i .. 4i+3, all query heads of one
-//    request and KV head: one index stream, one set of key gathers, two K
-//    MFMAs per frequency (pairs 0-1 and 2-3) on the same key column, and
-//    each V lane accumulates two query heads from one set of value gathers.
+//    request and KV head: one index stream, one set of key gathers, and each
+//    V lane accumulates two query heads from one set of value gathers.  As
+//    the four heads share each key, the lane rotates the key once (fp32, 4
+//    VALU operations per frequency instead of 8 for four heads) and the dot
+//    products with the four queries run as fp32 v_mfma_f32_4x4x1f32 products
+//    (row = head, column = position), all issued back to back after the
+//    rotations.
 //  * K side: a lane owns one position (of its 16-lane row) and one quarter
 //    of the RoPE frequencies.  For each frequency one v_mfma_f32_4x4x4f16 with
 //    the block-diagonal query matrix [[q0_f, q0_h], [q0_h, -q0_f]] (+) the same
@@ -377,8 +381,13 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      (x_f hi, x_h hi, x_f lo, x_h lo) against the key column
   //      (k_f, k_h, k_f, k_h) of one stream, so one product covers both pairs
   //      when they share keys and two (one per stream) when they do not.
-  half4v AK[F];
-  half4v AK2[G4 ? F : 1];                // G4: the same rows for pairs 2 and 3
+  half4v AK[G4 ? 1 : F];
+  //      G4: the quad's four query heads share one key per position, so the
+  //      lane rotates that key itself (fp32) and the matrix cores take the
+  //      dot products with fp32 operands: lane lb supplies head lb's query
+  //      at the quarter's channels f (AQ[i]) and f + D/2 (AQ[F + i]), one
+  //      v_mfma_f32_4x4x1f32 per channel against the rotated key's channel
+  float AQ[G4 ? 2 * F : 1];
   // TaSQ: u pair of the lane's i-th frequency slot: the pairs of its quarter's
   // lo groups, then those of its hi groups
   auto tq_upair = [&](int i) { return i < F / 2 ? la * (F / 2) + i : D / 4 + la * (F / 2) + (i - F / 2); };
@@ -413,18 +422,21 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     const int kk = s ? kq[1] : kq[0], bb = s ? bq[1] : bq[0];
     const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
     const size_t qoff = ((size_t)bb * p.H_q + jq) * D + la * F;
-    // G4: query head of pair 2 + s (clamped to a valid head of the request)
-    const int jq2 = h * p.grp + (okq_hi[s] ? kk + 2 - bb * p.grp : 0);
-    const size_t qoff2 = ((size_t)bb * p.H_q + jq2) * D + la * F;
+    if constexpr (G4) {
+      // head lb of the quad: pair kq[lb & 1] + (lb & 2), clamped to a valid
+      // head of the request when past the group's end
+      const bool okh = lb < 2 ? okq[lb] : okq_hi[lb - 2];
+      const int kh = kq[lb & 1] + (lb & 2), bh = bq[lb & 1];
+      const int jh = h * p.grp + (okh ? kh - bh * p.grp : 0);
+      const size_t qh = ((size_t)bh * p.H_q + jh) * D + la * F;
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        AQ[i] = u2f((uint32_t)((const uint16_t*)p.q)[qh + i] << 16);
+        AQ[F + i] = u2f((uint32_t)((const uint16_t*)p.q)[qh + D / 2 + i] << 16);
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      if constexpr (G4) {
-        const float a2 = u2f((uint32_t)((const uint16_t*)p.q)[qoff2 + i] << 16);
-        const float c2 = u2f((uint32_t)((const uint16_t*)p.q)[qoff2 + D / 2 + i] << 16);
-        const _Float16 g0 = (_Float16)((lb & 1) ? c2 : a2), g1 = (_Float16)((lb & 1) ? -a2 : c2);
-        const _Float16 zz = (_Float16)0.f;
-        AK2[i] = s ? (half4v){zz, zz, g0, g1} : (half4v){g0, g1, zz, zz};
-      }
       float a, c;
       if constexpr (QF32) {
         a = ((const float*)p.q)[qoff + i];
@@ -441,6 +453,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       } else {
         AK[i] = s ? (half4v){z, z, h0, h1} : (half4v){h0, h1, z, z};
       }
+    }
     }
   }
 
@@ -632,9 +645,37 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      matrix cores, then s = sum_f cos_f X_f + sin_f Y_f in fp32 (this
   //      lane's quarter; klo/khi and tb hold the step's entries and rows)
   auto k_side = [&](float* sc) {
-    float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
-    float sa2 = 0.f, sb2 = 0.f, sa3 = 0.f, sb3 = 0.f;   // G4: pairs 2 and 3
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (G4) {
+      // rotate the position's key (lo channel f, hi channel f + D/2 of each
+      // frequency) in fp32, then add AQ . RoPE(k) for the four heads on the
+      // matrix cores: row = head, column = position, one channel per product
+      // All rotations first, then the products back to back (four
+      // accumulators), which run on the matrix cores while the wave goes on
+      // to the next phase.
+      float rf[F], rh[F];
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        const int r = i / C, e = i % C;                      // entry and element of frequency i
+        const half2v wl = as_h2(klo[0][r].d[e >> 1]), wh = as_h2(khi[0][r].d[e >> 1]);
+        const float kf = (float)((e & 1) ? wl.y : wl.x), kh = (float)((e & 1) ? wh.y : wh.x);
+        const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
+        const float sn = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
+        rf[i] = fmaf(cs, kf, fmaf(-sn, kh, 0.f));          // RoPE(k)_f
+        rh[i] = fmaf(sn, kf, fmaf(cs, kh, 0.f));           // RoPE(k)_{f + D/2}
+      }
+      float4v a[4] = {zero, zero, zero, zero};
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        a[2 * (i & 1)] = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[i], rf[i], a[2 * (i & 1)], 0, 0, 0);
+        a[2 * (i & 1) + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[F + i], rh[i], a[2 * (i & 1) + 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * F, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * F, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sc[k] = (a[0][k] + a[2][k]) + (a[1][k] + a[3][k]);
+    } else {
+    float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
       float4v xy;
@@ -670,17 +711,6 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
           }
         } else {
           xy = __builtin_amdgcn_mfma_f32_4x4x4f16(AK[i], __builtin_bit_cast(half4v, (uint2v){w0, w1}), zero, 0, 0, 0);
-          if constexpr (G4) {
-            // pairs 2 and 3 on the same key column
-            const float4v xy2 =
-                __builtin_amdgcn_mfma_f32_4x4x4f16(AK2[i], __builtin_bit_cast(half4v, (uint2v){w0, w0}), zero, 0, 0, 0);
-            const float cs2 = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
-            const float sn2 = (i & 1) ? tb[i >> 1].w : tb[i >> 1].y;
-            sa2 = fmaf(cs2, xy2.x, sa2);
-            sb2 = fmaf(sn2, xy2.y, sb2);
-            sa3 = fmaf(cs2, xy2.z, sa3);
-            sb3 = fmaf(sn2, xy2.w, sb3);
-          }
         }
       }
       const float cs = (i & 1) ? tb[i >> 1].z : tb[i >> 1].x;
@@ -692,8 +722,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     // interleave: each MFMA is followed by VALU work (the next perms and this
     // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
-    constexpr int KMF = (TQ || QF32) ? (SHARE ? 1 : 2) : (G4 ? 2 : 1);
-    constexpr int KVALU = TQ ? 4 : (G4 ? 9 : 6);
+    constexpr int KMF = (TQ || QF32) ? (SHARE ? 1 : 2) : 1;
+    constexpr int KVALU = TQ ? 4 : 6;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, KMF, 0);
@@ -701,9 +731,6 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     sc[0] = sa0 + sb0;
     sc[1] = sa1 + sb1;
-    if constexpr (G4) {
-      sc[2] = sa2 + sb2;
-      sc[3] = sa3 + sb3;
     }
   };
   // sum over the four quarters (lanes 4 apart within the 16-lane row); lanes
