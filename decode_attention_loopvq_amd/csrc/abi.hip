@@ -434,6 +434,15 @@ static int split_impl(const loopvq_dims* dims, int32_t t, int32_t B, const void*
   p.scale_log2 = scale * 1.4426950408889634f;
   const bool qf32 = dims->io_dtype == LOOPVQ_DTYPE_F32;
   int grid = pl.grid;
+  if (tasq == nullptr && pl.quad && pl.shared_rope && B <= DECODE_SORT_MAX && pl.n_dg / 8 <= 64) {
+    // quads in order of decreasing work: about one workgroup per CU, each
+    // keeping its head's slices in LDS and walking the items of its ranks (a
+    // larger grid would only add workgroups that find no item)
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+      grid = dims->H_kv * std::min(pl.wg_per_head, std::max(1, ncu / dims->H_kv));
+  }
   if (tasq != nullptr && pl.quad) {
     // the TaSQ kernel serves duos: the plan's chunks (and so the workspace)
     // stay, with two waves per quad's pairs

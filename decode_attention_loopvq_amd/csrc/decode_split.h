@@ -175,6 +175,61 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   //      order from seq_lens), then leave at once if none of this workgroup's
   //      quads has positions in its chunk (nothing staged, nothing written)
   const bool sorted = G4 && p.B <= DECODE_SORT_MAX;
+  // with shared rows (eight quads per workgroup, one chunk) the workgroups
+  // take the (group of 8 quads, chunk) items in order of decreasing work: a
+  // group is 8 quads in length order, its work in chunk c is
+  // clamp(L - c*Lc, 0, Lc) positions (L its longest request).  Full chunks
+  // come first (group-major), then each group's last, partial chunk by
+  // decreasing size.  A workgroup keeps its head's slices in LDS and takes
+  // the items of ranks item_rank(0), item_rank(1), ... of its head: w,
+  // 2S - 1 - w, 2S + w, ... for workgroup w of the S of its head, which
+  // deals the items out largest first and evens out the workgroups' sums
+  const bool ordered = G4 && ST && sorted && p.n_dg / WAVES <= 64;
+  const int wg_stride = max(nb / p.H_kv, 1);   // workgroups per head (quads keep the hardware's order)
+  auto item_rank = [&](int r) { return r * wg_stride + ((r & 1) ? wg_stride - 1 - wgi : wgi); };
+  // wave 0 writes the (group, chunk) of the item of rank `it` to wg_item
+  // (group -1: no such item)
+  auto select_item = [&](int it) {
+    if constexpr (!G4) return;
+    if (threadIdx.x < 64) {
+      const int n_groups = p.n_dg / WAVES;
+      const int g = (int)threadIdx.x;
+      const int qpr = p.grp >> 2;
+      const int Lg = g < n_groups ? len_sorted[req_sorted[(WAVES * g) / qpr]] : 0;
+      const int fc = Lg / p.Lc, pr = Lg - fc * p.Lc;
+      // inclusive prefix of the full-chunk counts over the groups
+      int inc = fc;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d);
+        if (g >= d) inc += o;
+      }
+      const int FT = __shfl(inc, 63);
+      bool mine;
+      int cg;
+      if (it < FT) {
+        mine = it >= inc - fc && it < inc;
+        cg = it - (inc - fc);
+      } else {
+        // partial chunks: rank by (size desc, group asc)
+        int rank = 0;
+#pragma unroll
+        for (int o = 0; o < 64; ++o) {
+          const int po = __builtin_amdgcn_readlane(pr, o);
+          rank += (po > pr || (po == pr && o < g)) ? 1 : 0;
+        }
+        mine = pr > 0 && rank == it - FT;
+        cg = fc;
+      }
+      const uint64_t bal = __ballot(mine);
+      const int src = bal ? (int)__builtin_ctzll(bal) : 0;
+      const int cs = __shfl(cg, src);
+      if (g == 0) {
+        wg_item[0] = bal ? src : -1;
+        wg_item[1] = bal ? cs : 0;
+      }
+    }
+  };
   if constexpr (G4) {
     if (sorted) {
       // lengths padded with -1 to a multiple of 4 (padding ranks after every request)
@@ -195,54 +250,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         req_sorted[r] = t;
       }
     }
-    // with shared rows (eight quads per workgroup, one chunk) the workgroups
-    // take the (group of 8 quads, chunk) items in order of decreasing work:
-    // a group is 8 quads in length order, its work in chunk c is
-    // clamp(L - c*Lc, 0, Lc) positions (L its longest request).  Full chunks
-    // come first (group-major), then each group's last, partial chunk by
-    // decreasing size; the hardware starts workgroups in index order, so each
-    // round of workgroups holds items of similar size
-    if (threadIdx.x == 0) {
-      wg_busy = 0;
-      wg_item[0] = -1;
-      wg_item[1] = 0;
-    }
+    if (threadIdx.x == 0) wg_busy = 0;
     __syncthreads();
-    const int n_groups = p.n_dg / WAVES;
-    if (ST && sorted && n_groups <= 64) {
-      if (threadIdx.x < 64) {
-        const int g = (int)threadIdx.x;
-        const int qpr = p.grp >> 2;
-        const int Lg = g < n_groups ? len_sorted[req_sorted[(WAVES * g) / qpr]] : 0;
-        const int fc = Lg / p.Lc, pr = Lg - fc * p.Lc;
-        // inclusive prefix of the full-chunk counts over the groups
-        int inc = fc;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int o = __shfl_up(inc, d);
-          if (g >= d) inc += o;
-        }
-        const int F = __shfl(inc, 63);
-        const int it = wgi;
-        if (it < F) {
-          if (it >= inc - fc && it < inc) {
-            wg_item[0] = g;
-            wg_item[1] = it - (inc - fc);
-          }
-        } else {
-          // partial chunks: rank by (size desc, group asc)
-          int rank = 0;
-#pragma unroll
-          for (int o = 0; o < 64; ++o) {
-            const int po = __builtin_amdgcn_readlane(pr, o);
-            rank += (po > pr || (po == pr && o < g)) ? 1 : 0;
-          }
-          if (pr > 0 && rank == it - F) {
-            wg_item[0] = g;
-            wg_item[1] = fc;
-          }
-        }
-      }
+    if (ordered) {
+      select_item(item_rank(0));
       __syncthreads();
       if (wg_item[0] < 0) return;   // workgroup-uniform: no work left for this item number
     } else {
@@ -314,11 +325,13 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
   }
   __syncthreads();
 
+  // ---- the workgroup's items: one, or with ordered items every item of
+  //      ranks item_rank(0), item_rank(1), ... (the slices stay in LDS)
+  for (int rnd = 0;; ++rnd) {
   // ---- this wave's work item (wave-uniform): one duo of pairs, one chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   // G4 with shared rows and ordered items: group wg_item[0], chunk wg_item[1]
-  const bool ordered = G4 && ST && sorted && p.n_dg / WAVES <= 64;
   const int item = ordered ? (wg_item[1] * p.n_dg + wg_item[0] * WAVES + wave) : wgi * WAVES + wave;
   const bool item_ok = item < p.items_per_head;
   const int ch = item_ok ? item / p.n_dg : 0;
@@ -425,8 +438,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     if constexpr (G4) {
       // head lb of the quad: pair kq[lb & 1] + (lb & 2), clamped to a valid
       // head of the request when past the group's end
-      const bool okh = lb < 2 ? okq[lb] : okq_hi[lb - 2];
-      const int kh = kq[lb & 1] + (lb & 2), bh = bq[lb & 1];
+      const bool okh = (lb & 2) ? ((lb & 1) ? okq_hi[1] : okq_hi[0]) : ((lb & 1) ? okq[1] : okq[0]);
+      const int kh = ((lb & 1) ? kq[1] : kq[0]) + (lb & 2), bh = (lb & 1) ? bq[1] : bq[0];
       const int jh = h * p.grp + (okh ? kh - bh * p.grp : 0);
       const size_t qh = ((size_t)bh * p.H_q + jh) * D + la * F;
 #pragma unroll
@@ -1062,8 +1075,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int j = 0; j < HPL; ++j) {
     const int pj = G4 ? 2 * sv + j : sv;                   // pair of the wave
-    const bool okj = G4 ? (pj < 2 ? okq[pj] : okq_hi[pj - 2]) : okq[sv];
-    if (!(active && okj && rp == 0 && la == 0 && p0 < len[G4 ? 0 : sv])) continue;
+    const bool ok0 = (pj & 1) ? okq[1] : okq[0], ok1 = (pj & 1) ? okq_hi[1] : okq_hi[0];
+    const bool okj = G4 ? ((pj & 2) ? ok1 : ok0) : (sv ? okq[1] : okq[0]);
+    if (!(active && okj && rp == 0 && la == 0 && p0 < (G4 || sv == 0 ? len[0] : len[1]))) continue;
     const int kpair = G4 ? pair0 + pj : kq[sv];
     const size_t part = (size_t)(h * p.n_pairs + kpair) * p.n_chunks + ch;
     const float L = l[j];
@@ -1076,6 +1090,13 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       *(float4v*)(op + base) = acc[j][u] * inv;
     }
     if (lb == 0) p.part_lse[part] = L > 0.f ? m[j] + log2f(lx[j]) : -INFINITY;
+  }
+  if (!ordered) break;
+  // every wave is done with the ring, the page lists and wg_item
+  __syncthreads();
+  select_item(item_rank(rnd + 1));
+  __syncthreads();
+  if (wg_item[0] < 0) break;   // workgroup-uniform
   }
 }
 
