@@ -222,7 +222,11 @@ size_t loopvq_decode_workspace_bytes(const loopvq_dims* dims, int32_t B,
  *                 value; larger values become infinite scores); magnitudes
  *                 below 2^-14 are rounded to fp16 subnormals (an absolute
  *                 error below 2^-25).  fp32 queries are carried as two fp16
- *                 terms and need |q_i| below 65504 as well.
+ *                 terms and need |q_i| below 65504 as well.  (With a GQA
+ *                 group that is a multiple of four, bf16 queries and pages
+ *                 of 16 or more positions, the scores are taken in fp32
+ *                 and these limits do not bind; callers should not rely on
+ *                 that.)
  *   index_cache   the cache of block (t-1)/Tc.
  *   slices        [T][H_kv][2][K][c] fp16 from loopvq_build_codebook_slices.
  *   rope_table    device copy of loopvq_rope_table(max_pos, D, base).
