@@ -2,8 +2,9 @@
 wave) against the oracle, on the shapes that pick its code paths apart:
 workgroup items taken in order of decreasing work (shared RoPE rows), chunk
 edges, empty and one-token requests, a GQA group of eight (two quads per
-request), the bf16 sink and window over quads, and a batch too large to be
-put in length order (index order instead).
+request), the bf16 sink and window over quads, a batch too large to be put in
+length order (index order instead), and head counts for which each
+workgroup walks several items in turn.
 
 Bars as in the other decode tests: outputs within 2e-3 (+ half a bf16 ulp of
 the reference), lse within 1e-4 [LoopVQ paper, section "System
@@ -86,5 +87,22 @@ def test_quads_batch_beyond_the_length_order():
     lens[7] = 2000
     _note("quads, 520 requests")
     err, ratio = _check(cfg, lens, 66, t=1, requests=(0, 7, 100, 311, 519))
+    _note(f"max err {err:.2e} (bound ratio {ratio:.2f})")
+    assert ratio <= 1.0
+
+
+@pytest.mark.parametrize("H_kv,B", [(40, 16), (100, 8)])
+def test_quads_workgroups_walking_items(H_kv, B):
+    # ordered items walked by CUs // H_kv workgroups per head (6 and 2 on
+    # 256 CUs), so each workgroup takes several items in turn; 100 heads do
+    # not divide the CU count; lengths up to six chunks, some empty
+    cfg = synth.config_by_name("gqa_ragged").replace(H_kv=H_kv, H_q=4 * H_kv)
+    rng = np.random.default_rng(67 + H_kv)
+    lens = rng.integers(0, 2600, size=B).astype(np.int64)
+    lens[1] = 0
+    lens[2] = 1
+    lens[3] = 2600
+    _note(f"quads, H_kv={H_kv}, {B} requests, lens {lens.tolist()}")
+    err, ratio = _check(cfg, lens, 68 + H_kv, t=3, requests=tuple(range(B)), heads=(0, H_kv // 2 + 1, H_kv - 1))
     _note(f"max err {err:.2e} (bound ratio {ratio:.2f})")
     assert ratio <= 1.0
