@@ -350,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const int bs = duo / qpr;
       pair0 = (sorted ? req_sorted[min(bs, p.B - 1)] : bs) * p.grp + (duo - bs * qpr) * 4;
     }
-  #pragma unroll
+#pragma unroll
     for (int s = 0; s < 2; ++s) {
       kq[s] = pair0 + s;
       okq[s] = item_ok && kq[s] < p.n_pairs;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     }
     // G4: pairs 2 and 3 of the quad (the same request as pairs 0 and 1)
     bool okq_hi[2];
-  #pragma unroll
+#pragma unroll
     for (int s = 0; s < 2; ++s) okq_hi[s] = G4 && item_ok && pair0 + 2 + s < p.n_pairs;
     const int p0 = ch * p.Lc;
     const int lenx = max(len[0], len[1]);
@@ -374,12 +374,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     float m[HPL], l[HPL], lx[HPL];         // running max (log2 domain); sum of the rounded p
                                            // used in the products; exact sum of p (logsumexp)
     float4v acc[HPL][U];
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < HPL; ++j) {
       m[j] = -INFINITY;
       l[j] = 0.f;
       lx[j] = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < U; ++u) acc[j][u] = (float4v){0.f, 0.f, 0.f, 0.f};
     }
 
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const int jq = h * p.grp + (okq[s] ? kk - bb * p.grp : 0);
       const size_t qrow = ((size_t)bb * p.H_q + jq) * D;
       const float* wrow = p.tq_w + (size_t)h * D;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < F; ++i) {
         const int f = tq_freq(i);
         float a, c;
@@ -442,13 +442,13 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         const int kh = ((lb & 1) ? kq[1] : kq[0]) + (lb & 2), bh = (lb & 1) ? bq[1] : bq[0];
         const int jh = h * p.grp + (okh ? kh - bh * p.grp : 0);
         const size_t qh = ((size_t)bh * p.H_q + jh) * D + la * F;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < F; ++i) {
           AQ[i] = u2f((uint32_t)((const uint16_t*)p.q)[qh + i] << 16);
           AQ[F + i] = u2f((uint32_t)((const uint16_t*)p.q)[qh + D / 2 + i] << 16);
         }
       } else {
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < F; ++i) {
           float a, c;
           if constexpr (QF32) {
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     const uint32_t tbo = (uint32_t)((row * FP * 16 + la * 4 + lb) * 16);
     int lim[2], last[2];
     const int32_t* btb[2];
-  #pragma unroll
+#pragma unroll
     for (int s = 0; s < 2; ++s) {
       lim[s] = min(len[s], p0 + p.Lc);
       last[s] = max(len[s] - 1, 0);
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     // stream for the K row group and one for the V groups
     constexpr int NPG = SP ? NS : (P8U ? 2 * NS : NS + 1);
     auto page_at = [&](int st, int* pg) {
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < NS; ++s) {
         if constexpr (SP) {
           pg[s] = btb[s][(min(max(p0 + st * NT, lo[s]), last[s]) >> p.log2P) + vz];
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       if constexpr (SP) {
         const uint8_t* base[2];
         size_t slot0[2];
-  #pragma unroll
+#pragma unroll
         for (int s = 0; s < NS; ++s) {
           const uint32_t page = has[s] ? (uint32_t)__builtin_amdgcn_readfirstlane(raw_page[s]) : 0u;
           const uint32_t gs = (uint32_t)(min(p0 + st * NT, last[s]) & ~(NT - 1)) & (uint32_t)(P - 1);
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         // are in bounds and masked)
         const uint8_t* vb[2];
         size_t vs[2];
-  #pragma unroll
+#pragma unroll
         for (int s = 0; s < NS; ++s) {
           const uint32_t pga = has[s] ? (uint32_t)__builtin_amdgcn_readfirstlane(raw_page[2 * s]) : 0u;
           const uint32_t pgb = has[s] ? (uint32_t)__builtin_amdgcn_readfirstlane(raw_page[2 * s + 1]) : 0u;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         vbase = (NS == 1 || sv == 0) ? vb[0] : vb[NS - 1];
         vslot = (NS == 1 || sv == 0) ? vs[0] : vs[NS - 1];
       } else {
-  #pragma unroll
+#pragma unroll
         for (int s = 0; s < NS; ++s) {
           const uint32_t page = has[s] ? (uint32_t)raw_page[s] : 0u;
           const uint32_t gs = (uint32_t)(min(p0 + st * NT + 4 * row, last[s]) & ~3) & (uint32_t)(P - 1);
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         const int f = tq_freq(i);
         return (uint32_t)(((f % F) >> 1) * 256 + (f / F) * 64 + (f & 1) * 8);
       };
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < FP; ++j) toff[j] = off(2 * j) | (off(2 * j + 1) << 16);
     }
     const uint32_t tbo_row = (uint32_t)((row * FP * 16 + lb) * 16);
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const int gt = min(p0 + st * NT, glast);
       if constexpr (TQ && !ST) {
         const uint8_t* tr = (const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo_row;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < FP; ++j) {
           const float2v a = *(const float2v*)(tr + (toff[j] & 0xffffu));
           const float2v b = *(const float2v*)(tr + (toff[j] >> 16));
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         }
       } else {
         const float4v* tr = (const float4v*)((const uint8_t*)p.rope + (size_t)(gt >> 2) * FP * 256 + tbo);
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < FP; ++j) tb[j] = tr[j * 16];
       }
     };
@@ -639,18 +639,18 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     // gathered K slice entries per stream, V entries per V position slot
     Entry<EB> klo[NS][Q], khi[NS][Q], ve[2][2 * Q];
     auto gather_k = [&](uint32_t (*kw)[LW]) {
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < NS; ++s)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < Q; ++r) {
           klo[s][r] = lds_entry<EB>(lds, entry_addr(kw[s], r, koff));
           khi[s][r] = lds_entry<EB>(lds, entry_addr(kw[s], Q + r, koff));
         }
     };
     auto gather_v = [&](uint32_t (*vw)[LW]) {
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < 2; ++t)
-  #pragma unroll
+#pragma unroll
         for (int sl = 0; sl < 2 * Q; ++sl) ve[t][sl] = lds_entry<EB>(lds, entry_addr(vw[t], sl, voff));
     };
 
@@ -667,7 +667,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         // back (four accumulators): an MFMA that waits for the rotation just
         // before it stalls the wave.
         float rf[F], rh[F];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < F; ++i) {
           const int r = i / C, e = i % C;                      // entry and element of frequency i
           const half2v wl = as_h2(klo[0][r].d[e >> 1]), wh = as_h2(khi[0][r].d[e >> 1]);
@@ -678,18 +678,18 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
           rh[i] = fmaf(sn, kf, fmaf(cs, kh, 0.f));           // RoPE(k)_{f + D/2}
         }
         float4v a[4] = {zero, zero, zero, zero};
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < F; ++i) {
           a[2 * (i & 1)] = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[i], rf[i], a[2 * (i & 1)], 0, 0, 0);
           a[2 * (i & 1) + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[F + i], rh[i], a[2 * (i & 1) + 1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x002, 4 * F, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * F, 0);
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < 4; ++k) sc[k] = (a[0][k] + a[2][k]) + (a[1][k] + a[3][k]);
       } else {
         float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < F; ++i) {
           float4v xy;
           if constexpr (TQ) {
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         // frequency's FMAs); issuing all MFMAs first would hold every X, Y live
         constexpr int KMF = (TQ || QF32) ? (SHARE ? 1 : 2) : 1;
         constexpr int KVALU = TQ ? 4 : 6;
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < F; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, KMF, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, KVALU, 0);
@@ -754,14 +754,14 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         // quarter la exposes pair la; the V lane pulls pairs 2*sv, 2*sv + 1 at
         // its two positions: sv2[2*j + e] = score of head j at position e
         float v[4];
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < 4; ++k) {
           v[k] = sc[k];
           v[k] += u2f(__builtin_amdgcn_mov_dpp(f2u(v[k]), 0x124, 0xf, 0xf, true));   // row_ror:4
           v[k] += u2f(__builtin_amdgcn_mov_dpp(f2u(v[k]), 0x128, 0xf, 0xf, true));   // row_ror:8
         }
         const uint32_t ex = f2u(la == 0 ? v[0] : (la == 1 ? v[1] : (la == 2 ? v[2] : v[3])));
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < 4; ++k) sv2[k] = u2f(__builtin_amdgcn_ds_bpermute(bperm_g4 + 16 * (k >> 1) + 4 * (k & 1), ex));
         return;
       }
@@ -781,7 +781,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     auto v_side = [&](int g0, const float* sv2, uint32_t sg) {
       const int posa = g0 + vrel;
       const bool va = (uint32_t)posa < vspan, vb = (uint32_t)(posa + 1) < vspan;
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < HPL; ++j) {      // G4: the lane's two query heads share the V gathers
         float s0 = sv2[2 * j], s1 = sv2[2 * j + 1];
         if constexpr (TQ) {
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
             const float fct = __builtin_amdgcn_exp2f(m[j] - smax);
             l[j] *= fct;
             lx[j] *= fct;
-  #pragma unroll
+#pragma unroll
             for (int u = 0; u < U; ++u) acc[j][u] *= fct;
             m[j] = smax;
           }
@@ -808,7 +808,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         lx[j] += pa + pb;
         half4v A[2], Alo[2];
         const float pv[2] = {pa, pb};
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 2; ++t) {
           const _Float16 ph = (_Float16)pv[t];
           const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
@@ -824,9 +824,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
           }
         }
         float4v* ac = acc[j];
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 2; ++t) {
-  #pragma unroll
+#pragma unroll
           for (int sl = 0; sl < 2 * Q; ++sl) {
             if constexpr (EB == 8) {
               const half4v Bv = __builtin_bit_cast(half4v, (uint2v){ve[t][sl].d[0], ve[t][sl].d[1]});
@@ -914,7 +914,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       // capped at pcnt - 1; clamping commutes with the shift, so per step it is
       // min(max(x / P - pa, plo), phi) with one shift shared by the streams
       int pa[2], plo[2], phi[2];
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < NS; ++s) {
         pa[s] = min(max(p0, lo[s]), last[s]) >> p.log2P;
         const int pcnt = max(min((min(p0 + p.Lc - 1, last[s]) >> p.log2P) - pa[s] + 1, PGMAX), 1);
@@ -925,7 +925,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       if (lane == 0) wsteps[wave] = my_steps;
       __syncthreads();
       int nst = 0;
-  #pragma unroll
+#pragma unroll
       for (int w = 0; w < WAVES; ++w) nst = max(nst, wsteps[w]);
       nst = (nst + 3) & ~3;                    // four steps per iteration (ring x row buffers)
       constexpr int PIECES = TSTEP / 16 / WAVES;   // 16-byte pieces per wave and step
@@ -964,7 +964,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       };
       auto table_lds = [&](int st) {
         const uint8_t* ring = lds + LDS_SLICES + (st & 1) * TSTEP + tbo;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < FP; ++j) tb[j] = *(const float4v*)(ring + j * 256);
       };
       // this wave's LDS writes are done, then the workgroup meets
@@ -976,7 +976,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       };
       // page ids of step st (uniform values, clamped into the chunk's list)
       auto page_lds = [&](int st, int* pg) {
-  #pragma unroll
+#pragma unroll
         for (int s = 0; s < NS; ++s)
           pg[s] = plist[s * PGMAX + min(max(((p0 + st * NT) >> p.log2P) - pa[s], plo[s]), phi[s])];
       };
@@ -1038,41 +1038,53 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     // ---- merge the 8 position slots of each (pair, quarter) and write the
     //      chunk's partials.  The slots of one (pair, quarter) are the lanes of
     //      rows 2*sv, 2*sv + 1 at slots la = 0..3 of one quarter lb: 4 and 8
-    //      lanes apart inside a row and 16 apart across the two rows.  Three
-    //      exchange rounds (DPP row rotations by 4 and 8, then a swizzle that
-    //      swaps the two rows) leave the merged state in each of the 8 lanes;
-    //      every wave merges its own lanes, so no barrier or LDS is involved.
+    //      lanes apart inside a row and 16 apart across the two rows.  The
+    //      merged state has M = the largest m of the 8 slots and sums weighted
+    //      by 2^(m - M) (0 for an empty slot: l = 0, m = -inf).  Three exchange
+    //      rounds (DPP row rotations by 4 and 8, then a swizzle that swaps the
+    //      two rows) give M in each lane; each lane scales its own state once,
+    //      and three more rounds add the scaled states, the rotations fused
+    //      into the adds.  Every wave merges its own lanes: no barrier, no LDS.
     auto xchg = [&](float v, int round) -> float {
       if (round == 0) return u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x124, 0xf, 0xf, true));   // row_ror:4
       if (round == 1) return u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x128, 0xf, 0xf, true));   // row_ror:8
       return u2f(__builtin_amdgcn_ds_swizzle(f2u(v), 0x401f));                                // lane ^ 16
     };
-  #pragma unroll
+    float mm[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      float M = m[j];
+#pragma unroll
+      for (int round = 0; round < 3; ++round) M = fmaxf(M, xchg(M, round));
+      const float w = l[j] > 0.f ? __builtin_amdgcn_exp2f(m[j] - M) : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[j][u] *= w;
+      l[j] *= w;
+      lx[j] *= w;
+      mm[j] = M;
+    }
+#pragma unroll
     for (int round = 0; round < 3; ++round) {
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < HPL; ++j) {
-        const float mo = xchg(m[j], round), lo2 = xchg(l[j], round), lxo = xchg(lx[j], round);
-        // an empty state (no positions yet: l = 0, m = -inf) carries weight 0
-        const float M = fmaxf(m[j], mo);
-        const float w1 = l[j] > 0.f ? __builtin_amdgcn_exp2f(m[j] - M) : 0.f;
-        const float w2 = lo2 > 0.f ? __builtin_amdgcn_exp2f(mo - M) : 0.f;
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < U; ++u) {
           float4v a = acc[j][u];
-          a.x = fmaf(w2, xchg(a.x, round), w1 * a.x);
-          a.y = fmaf(w2, xchg(a.y, round), w1 * a.y);
-          a.z = fmaf(w2, xchg(a.z, round), w1 * a.z);
-          a.w = fmaf(w2, xchg(a.w, round), w1 * a.w);
+          a.x += xchg(a.x, round);
+          a.y += xchg(a.y, round);
+          a.z += xchg(a.z, round);
+          a.w += xchg(a.w, round);
           acc[j][u] = a;
         }
-        l[j] = fmaf(w2, lo2, w1 * l[j]);
-        lx[j] = fmaf(w2, lxo, w1 * lx[j]);
-        m[j] = l[j] > 0.f ? M : -INFINITY;
+        l[j] += xchg(l[j], round);
+        lx[j] += xchg(lx[j], round);
       }
     }
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) m[j] = l[j] > 0.f ? mm[j] : -INFINITY;
     // one lane per (pair, quarter) writes: row 2*sv, position slot la == 0
     // (G4: for each of its two query heads, pairs 2*sv and 2*sv + 1 of the quad)
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < HPL; ++j) {
       const int pj = G4 ? 2 * sv + j : sv;                   // pair of the wave
       const bool ok0 = (pj & 1) ? okq[1] : okq[0], ok1 = (pj & 1) ? okq_hi[1] : okq_hi[0];
@@ -1083,7 +1095,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
       const float L = l[j];
       const float inv = L > 0.f ? 1.f / L : 0.f;
       float* op = p.part_o + part * D;
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < U; ++u) {
         const int lc = 4 * u;
         const int base = lc < F ? lb * F + lc : D / 2 + lb * F + (lc - F);
