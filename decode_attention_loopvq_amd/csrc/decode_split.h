@@ -677,16 +677,16 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
           rf[i] = fmaf(cs, kf, fmaf(-sn, kh, 0.f));          // RoPE(k)_f
           rh[i] = fmaf(sn, kf, fmaf(cs, kh, 0.f));           // RoPE(k)_{f + D/2}
         }
-        float4v a[4] = {zero, zero, zero, zero};
+        float4v a0 = zero, a1 = zero;
 #pragma unroll
         for (int i = 0; i < F; ++i) {
-          a[2 * (i & 1)] = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[i], rf[i], a[2 * (i & 1)], 0, 0, 0);
-          a[2 * (i & 1) + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[F + i], rh[i], a[2 * (i & 1) + 1], 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[i], rf[i], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(AQ[F + i], rh[i], a1, 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x002, 4 * F, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * F, 0);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sc[k] = (a[0][k] + a[2][k]) + (a[1][k] + a[3][k]);
+        for (int k = 0; k < 4; ++k) sc[k] = a0[k] + a1[k];
       } else {
         float sa0 = 0.f, sb0 = 0.f, sa1 = 0.f, sb1 = 0.f;
 #pragma unroll
