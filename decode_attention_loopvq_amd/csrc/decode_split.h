@@ -476,6 +476,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
     const uint32_t voff = PG ? (uint32_t)((N + lb * Q) * KENT * EB) : (uint32_t)(KENT * 256) + koff;
     const uint32_t asel0 = lb == 0 ? 0x0c0c0100u : (lb == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
     const uint32_t asel1 = lb == 2 ? 0x0c0c0100u : (lb == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
+    // the same for the high half of a packed pair of fp16 values
+    const uint32_t asel2 = lb == 0 ? 0x0c0c0302u : (lb == 1 ? 0x03020c0cu : 0x0c0c0c0cu);
+    const uint32_t asel3 = lb == 2 ? 0x0c0c0302u : (lb == 3 ? 0x03020c0cu : 0x0c0c0c0cu);
     // K-role lanes holding my V positions 8*rp + 2*la (+1): row 2*rp + la/2,
     // position slots 2*(la%2) (+1); quarters 2*sv, 2*sv + 1 expose pair sv's
     // score after the quarter sum
@@ -795,11 +798,14 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         const bool need = smax > m[j] + LAZY_TAU;
         if (__ballot(need) != 0) {
           if (need) {
-            const float fct = __builtin_amdgcn_exp2f(m[j] - smax);
-            l[j] *= fct;
-            lx[j] *= fct;
+            // a state with no position yet (m = -inf) holds zeros: only m moves
+            if (m[j] != -INFINITY) {
+              const float fct = __builtin_amdgcn_exp2f(m[j] - smax);
+              l[j] *= fct;
+              lx[j] *= fct;
 #pragma unroll
-            for (int u = 0; u < U; ++u) acc[j][u] *= fct;
+              for (int u = 0; u < U; ++u) acc[j][u] *= fct;
+            }
             m[j] = smax;
           }
         }
@@ -807,21 +813,27 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         const float pb = vb ? __builtin_amdgcn_exp2f(sb - m[j]) : 0.f;
         lx[j] += pa + pb;
         half4v A[2], Alo[2];
-        const float pv[2] = {pa, pb};
+        if constexpr (QF32) {
+          const float pv[2] = {pa, pb};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const _Float16 ph = (_Float16)pv[t];
-          const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
-          A[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
-          // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
-          if constexpr (QF32) {
+          for (int t = 0; t < 2; ++t) {
+            const _Float16 ph = (_Float16)pv[t];
+            const uint32_t pbits = (uint32_t)__builtin_bit_cast(uint16_t, ph);
+            A[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pbits, asel0), perm(0u, pbits, asel1)});
+            // fp32 output: p = fp16 high part + fp16 low part, two MFMAs per unit
             const _Float16 pl = (_Float16)(pv[t] - (float)ph);
             const uint32_t lbits = (uint32_t)__builtin_bit_cast(uint16_t, pl);
             Alo[t] = __builtin_bit_cast(half4v, (uint2v){perm(0u, lbits, asel0), perm(0u, lbits, asel1)});
             l[j] += (float)ph + (float)pl;
-          } else {
-            l[j] += (float)ph;
           }
+        } else {
+          // both p rounded to fp16 in one packed word; l adds the same two
+          // values with one dot product against (1, 1)
+          const half2v ph2 = (half2v){(_Float16)pa, (_Float16)pb};
+          const uint32_t pw = __builtin_bit_cast(uint32_t, ph2);
+          A[0] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pw, asel0), perm(0u, pw, asel1)});
+          A[1] = __builtin_bit_cast(half4v, (uint2v){perm(0u, pw, asel2), perm(0u, pw, asel3)});
+          l[j] = __builtin_amdgcn_fdot2(ph2, (half2v){(_Float16)1.f, (_Float16)1.f}, l[j], false);
         }
         float4v* ac = acc[j];
 #pragma unroll
