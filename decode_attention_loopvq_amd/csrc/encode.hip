@@ -41,7 +41,7 @@
 
 namespace loopvq {
 
-template <int G, int C, bool XF32, int BITS, bool PAGED, bool PG, bool NTC>
+template <int G, int C, bool XF32, int BITS, bool PAGED, bool PG, bool NTC, bool ONE>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   constexpr int KD = XF32 ? 2 * G : G;          // reduction length (fp32: high and low halves)
   constexpr int KDP = KD < 16 ? 16 : KD;        // padded to the MFMA depth
@@ -134,7 +134,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       run_off[mu][q] = (size_t)(beta * Tc + m) * step_stride + (size_t)hd * head_stride + i0;
     }
   // raw input words of one unit (bf16 pairs or fp32), converted at use
-  struct Raw { uint32_t w[NMF][NRUN][RW]; };
+  // (with a unit inside one token, also that token's slot: a scalar load from
+  // the constant address space, so its wait never holds on vector loads)
+  struct Raw { uint32_t w[NMF][NRUN][RW]; int slot; };
+  typedef __attribute__((address_space(4))) const int cint4;
   // dense input with n <= 32 groups per token: a unit is 32/n whole tokens and
   // a lane keeps its group, so its offset advances by a wave-uniform step per
   // unit (no per-lane multiplies); the last, partial unit takes the clamped path
@@ -142,6 +145,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
   const size_t lane_off0 = (size_t)(col >> (ln <= 5 ? ln : 0)) * H * D + (size_t)(col & (n - 1)) * C;
   const size_t unit_step = (size_t)(32 >> (ln <= 5 ? ln : 0)) * H * D;
   auto load_raw = [&](int u, Raw& r) {
+    if constexpr (ONE)
+      r.slot = ((cint4*)(uintptr_t)p.slot_mapping)[__builtin_amdgcn_readfirstlane((min(u, nunit - 1) << 5) >> ln)];
     size_t voff;
     if (incr && u * 32 + 31 < nvec) {
       voff = lane_off0 + (size_t)u * unit_step;
@@ -241,7 +246,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     const bool vok = v < nvec;
     const int vc = vok ? v : nvec - 1;
     const int tok = PG ? vc : vc >> ln, g = PG ? gq : vc & (n - 1);
-    const int slot = p.slot_mapping[tok];
+    // with 32 or more groups per token (and one codebook for all groups) a
+    // unit lies inside one token, whose slot is then one scalar load and whose
+    // row address is scalar arithmetic
+    int slot_s = 0, slot_v = 0;
+    if constexpr (ONE) slot_s = cur.slot;
+    else slot_v = p.slot_mapping[tok];
     // ---- scores against all entries: per 32-entry tile a lane holds 16
     //      entries (rows 8q + 4*hf + s) of its vector.  It keeps the best tile
     //      (strict compare of the tile maxima in increasing tile order) and
@@ -334,15 +344,22 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
     // ---- write the code into its row slot
     // byte of the code: page, row in the page (rows are a power of two of
     // bytes), slot byte; unsigned 32-bit parts and one 32 x 32 -> 64 product
-    const uint32_t us = (uint32_t)slot;
-    const uint32_t sl = (uint32_t)(fixed_group ? sl_lane : slot_of(g));
-    uint8_t* const code = head_rows + ((uint64_t)(us >> p.log2P) * page_bytes +
-                                       (((us & (uint32_t)(P - 1)) << lr) + (BITS == 8 ? sl : sl >> 1)));
-    if constexpr (BITS == 8) {
-      if (hf == 0 && vok) *code = (uint8_t)bidx;
+    auto row_of = [&](uint32_t us) {
+      return head_rows + ((uint64_t)(us >> p.log2P) * page_bytes + ((us & (uint32_t)(P - 1)) << lr));
+    };
+    auto put = [&](uint8_t* row, uint32_t sl, bool ok) {
+      if constexpr (BITS == 8) {
+        if (hf == 0 && ok) row[sl] = (uint8_t)bidx;
+      } else {
+        const int other = __shfl_xor(bidx, 1);
+        if (hf == 0 && ok && (col & 1) == 0) row[sl >> 1] = (uint8_t)((bidx & 15) | ((other & 15) << 4));
+      }
+    };
+    if constexpr (ONE) {
+      // every vector of the unit exists (the vector count is a multiple of 32)
+      put(row_of((uint32_t)slot_s), (uint32_t)(ln == 5 ? sl_lane : slot_of(v & (n - 1))), true);
     } else {
-      const int other = __shfl_xor(bidx, 1);
-      if (hf == 0 && vok && (col & 1) == 0) *code = (uint8_t)((bidx & 15) | ((other & 15) << 4));
+      put(row_of((uint32_t)slot_v), (uint32_t)(fixed_group ? sl_lane : slot_of(g)), vok);
     }
   };
   int u = u0;
@@ -360,19 +377,25 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
 template <int G, int C, bool XF32, int BITS, bool PG>
 static hipError_t launch_encode_pg(const EncodeParams& p, int n_blocks, hipStream_t s) {
   dim3 grid(p.n_unit_groups, n_blocks * p.kv_n * p.H_kv * (PG ? p.D / C : 1));
+  // 32 or more groups per token (one codebook for all): a unit of 32 vectors
+  // lies inside one token
+  const bool one = !PG && p.D / C >= 32;
   if constexpr (!XF32) {
     // bf16 window pages (decode-time page encoding); no near-tie count there
     if (p.src_slot != nullptr) {
       if (p.near_tie != nullptr) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true, PG, false>), grid, dim3(256), 0, s, p);
+      if (one) hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true, PG, false, !PG>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, true, PG, false, false>), grid, dim3(256), 0, s, p);
       return hipGetLastError();
     }
   }
   if (p.src_slot != nullptr) return hipErrorInvalidValue;
   if (p.near_tie != nullptr)
-    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, true>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, true, false>), grid, dim3(256), 0, s, p);
+  else if (one)
+    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, false, !PG>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((encode_kernel<G, C, XF32, BITS, false, PG, false, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -16,7 +16,9 @@ index sets put the copies
   * with 4-bit codes (one 16-row tile);
 
 and run through every encoder instance: bf16 and fp32 input, c = 2, 4, 8,
-eight blocks, one codebook per channel group, bf16 window pages, TaSQ keys.
+16, 32 and 64 groups per token (a unit of 32 vectors spans two tokens, one
+token or half a token), eight blocks, one codebook per channel group, bf16
+window pages, TaSQ keys.
 
 A vector is compared exactly unless two *distinct* entries lie within the
 oracle's near-tie band of each other (then it is left out and counted).  The
@@ -150,6 +152,7 @@ def _encode_dense(cfg, dims, cb, xk, xv, slots, npg, count_ties=True):
 
 @pytest.mark.parametrize("name,over,n_tok", [
     ("layer1p4b", dict(H_kv=2, H_q=2), 300),           # bf16, c = 4, G = 16, 8-bit
+    ("layer1p4b", dict(H_kv=2, H_q=2, c=2, Tc=8, T=8, rhos=(0.8,) * 7), 300),   # 64 groups per token
     ("gqa_ragged", dict(H_kv=2, H_q=8), 200),          # bf16, c = 8, G = 32
     ("tiny", dict(), 256),                             # fp32, c = 2, 4-bit (one 16-row tile)
     ("tiny", dict(bits=8), 256),                       # fp32, G = 8, 8-bit
