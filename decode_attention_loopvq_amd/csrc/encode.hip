@@ -274,24 +274,20 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
       for (int mu = 0; mu < NMF; ++mu) d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[t][mu], Bv[mu], d, 0, 0, 0);
       return d;
     };
-    // the tile's maximum; a strictly larger one makes it the best tile
+    // the running maximum taken over the tile's scores; it grows exactly when
+    // the tile's maximum is strictly larger, which makes it the best tile
     auto keep_best = [&](int t, const float16v& d) {
-      float m = __builtin_fmaxf(__builtin_fmaxf(d[0], d[1]), d[2]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, d[3]), d[4]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, d[5]), d[6]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, d[7]), d[8]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, d[9]), d[10]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, d[11]), d[12]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, d[13]), d[14]);
-      m = __builtin_fmaxf(m, d[15]);
+      float m = best;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, d[r]), d[r + 1]);
       // a masked branch copies the scores (64-bit moves) instead of selecting
       // all 16 every tile; some lane of the wave takes it at almost every tile
       if (m > best) {
         __asm__ __volatile__("");          // keeps this a masked branch (no selects)
-        best = m;
         btile = t;
         bd = d;
       }
+      best = m;
     };
     // the MFMA of tile t+1 is issued before the search of tile t (whose
     // masked branch ends a basic block), so the matrix core runs during it
