@@ -51,17 +51,20 @@ METRIC = "decode-attn cached tokens/s (all heads, 1 loop step) @32K ctx; encode 
 DECODE_KERNEL = "decode_split_kernel"
 
 
-def _source_sha() -> str:
+def _source_sha(files=("decode_split.h", "decode.hip", "common.h", "kernels.h")) -> str:
     h = hashlib.sha256()
-    for f in ("decode_split.h", "decode.hip", "common.h", "kernels.h"):
+    for f in files:
         with open(os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _traffic_from_profile(sha: str):
+ENCODE_SOURCES = ("encode.hip", "common.h", "kernels.h")
+
+
+def _traffic_from_profile(sha: str, name: str = "decode_split_longctx32k_pmc.json"):
     """HBM bytes per launch from committed PMC counters, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_split_longctx32k_pmc.json")
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -570,7 +573,9 @@ def bench_encode_cfg(args, torch, np, synth, lv, name):
             "workload": f"{cfg.name}: prefill encode of {cfg.encode_batch} x {cfg.encode_tokens} tokens, "
                         f"{cfg.n_blocks} block(s), H_kv={cfg.H_kv}, D={cfg.D}, c={cfg.c}, Tc={cfg.Tc}, K={cfg.K}",
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": (_traffic_from_profile(_source_sha(ENCODE_SOURCES), "encode_layer1p4b_pmc.json")
+                                     if name == "layer1p4b" else None),
                          "kernel": "encode_kernel", "algorithmic_flops_per_launch": flops}}
 
 
