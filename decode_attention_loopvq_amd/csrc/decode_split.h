@@ -26,8 +26,8 @@
 //    the four heads share each key, the lane rotates the key once (fp32, 4
 //    VALU operations per frequency instead of 8 for four heads) and the dot
 //    products with the four queries run as fp32 v_mfma_f32_4x4x1f32 products
-//    (row = head, column = position), all issued back to back after the
-//    rotations.
+//    (row = head, column = position), issued after the rotations into two
+//    accumulators that are summed once.
 //  * K side: a lane owns one position (of its 16-lane row) and one quarter
 //    of the RoPE frequencies.  For each frequency one v_mfma_f32_4x4x4f16 with
 //    the block-diagonal query matrix [[q0_f, q0_h], [q0_h, -q0_f]] (+) the same
@@ -674,9 +674,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeParams p) {
         // rotate the position's key (lo channel f, hi channel f + D/2 of each
         // frequency) in fp32, then add AQ . RoPE(k) for the four heads on the
         // matrix cores: row = head, column = position, one channel per
-        // product.  All rotations come first and the products follow back to
-        // back (four accumulators): an MFMA that waits for the rotation just
-        // before it stalls the wave.
+        // product.  All rotations come first and the products follow, the
+        // lo-channel and hi-channel products in two accumulators (one wait
+        // state between the paired MFMAs, 4 adds to sum them): an MFMA that
+        // waits for the rotation just before it stalls the wave, and one
+        // accumulator makes a chain of dependent MFMAs.
         float rf[F], rh[F];
 #pragma unroll
         for (int i = 0; i < F; ++i) {
