@@ -34,9 +34,14 @@ def _pools_from_dense(xk, xv, n_pages, src_slot):
     return pools
 
 
-@pytest.mark.parametrize("name,n_tok", [("layer1p4b", 200), ("deeploop", 64), ("gqa_ragged", 72)])
-def test_encode_pages_equals_dense_encode(name, n_tok):
-    cfg = synth.config_by_name(name)
+@pytest.mark.parametrize("name,over,n_tok", [
+    ("layer1p4b", dict(), 200),
+    ("deeploop", dict(), 64),
+    ("gqa_ragged", dict(), 72),                                  # 16 groups per token
+    ("layer1p4b", dict(c=2, Tc=8, T=8, rhos=(0.8,) * 7, H_kv=2, H_q=2), 120),   # 64 groups per token
+])
+def test_encode_pages_equals_dense_encode(name, over, n_tok):
+    cfg = synth.config_by_name(name).replace(**over)
     xk, xv = synth.make_kv(cfg, n_tok, seed=cfg.index + 70)
     cb = synth.make_codebooks(cfg.replace(n_calib=400))
     lens = np.array([n_tok])
@@ -59,7 +64,7 @@ def test_encode_pages_equals_dense_encode(name, n_tok):
     got = paged.cpu().numpy()
     assert np.array_equal(got, dense.cpu().numpy()), "paged and dense inputs must give the same codes"
     ties, bad = check_codes(cfg, got, xk, xv, cb, slots, heads=[0, cfg.H_kv - 1])
-    _note(f"{name} page encode: near-ties {ties}, mismatches outside the band {bad}")
+    _note(f"{name} {over} page encode: near-ties {ties}, mismatches outside the band {bad}")
     assert bad == 0
 
 

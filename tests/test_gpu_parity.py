@@ -320,6 +320,32 @@ def test_fp32_io_paths(over, lens):
     assert err < 1e-4
 
 
+def test_two_channels_eight_steps_64_groups_per_token():
+    # c = 2 channels over Tc = 8 loop steps (G = 16): 64 groups per token, so
+    # a 32-vector encoder unit is half a token (the one-token instance with
+    # per-unit row slots) and an index row holds 64 codes
+    cfg = synth.config_by_name("layer1p4b").replace(c=2, Tc=8, T=8, rhos=(0.8,) * 7, H_kv=2, H_q=2)
+    lens = np.array([300, 45])
+    ntot = int(lens.sum())
+    xk, xv = synth.make_kv(cfg, ntot, seed=5)
+    cb = synth.make_codebooks(cfg.replace(n_calib=300))
+    bt, npg = synth.make_block_table(cfg, lens)
+    slots = np.concatenate([synth.slot_mapping_for(bt, b, int(n), cfg.page_size) for b, n in enumerate(lens)])
+    layer = GpuLayer(cfg, cb, int(lens.max()))
+    got = _encode_gpu(cfg, layer, xk, xv, slots, npg)
+    ties, bad = check_codes(cfg, got, xk, xv, cb, slots)
+    _note(f"c=2 Tc=8 encode: near-ties {ties}, mismatches outside the band {bad}")
+    assert bad == 0
+    ref_cache, _ = make_cache_from_data(cfg, xk, xv, cb, lens, bt, npg)
+    for t in (1, 5, 8):
+        q = synth.make_queries(cfg, len(lens), t=t)
+        o, lse = layer.decode(t, q, ref_cache[0], bt, lens)
+        ref = ref_decode(cfg, t, q, ref_cache[0], bt, lens, cb)
+        err, ratio = compare(cfg, o, lse, ref, lens)
+        _note(f"c=2 Tc=8 decode t={t}: max err {err:.2e} (bound ratio {ratio:.2f})")
+        assert ratio <= 1.0
+
+
 def test_per_step_coding_runs_on_the_same_kernels():
     # Tc = 1: every loop step has its own codebook and its own cache block
     cfg = synth.config_by_name("layer1p4b").replace(Tc=1, c=8, H_kv=2, H_q=2,
