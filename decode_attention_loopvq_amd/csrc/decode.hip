@@ -17,11 +17,29 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
   const int pq = blockIdx.x;
   const int b = pq / p.H_q, jq = pq - b * p.H_q;
   const int h = jq / p.grp, k = b * p.grp + (jq - h * p.grp);
-  const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
-  const int npart = len > 0 ? (len + p.Lc - 1) / p.Lc : 0;
   const size_t base = (size_t)(h * p.n_pairs + k) * p.n_chunks;
   const size_t wpart = (size_t)h * p.n_pairs + k;
   const int c0l = (int)threadIdx.x * CPL;    // the lane's first channel
+  // a batch's loads depend on the plan's chunk count only (indices clamped
+  // into it, no branches), so the first batch goes out together with the
+  // seq_lens read instead of after it; chunks at or past the request's own
+  // count are dropped once that count is known
+  // (lane i of the first NB reads the lse of chunk cb + i: a vector load,
+  // which goes out with the value loads; scalar loads would wait behind the
+  // seq_lens read)
+  float lel, le[NB], o[NB][CPL];
+  auto load_batch = [&](int cb) {
+    lel = p.part_lse[base + min(cb + ((int)threadIdx.x & (NB - 1)), p.n_chunks - 1)];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float* op = p.part_o + (base + min(cb + i, p.n_chunks - 1)) * D + c0l;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[i][c] = op[c];
+    }
+  };
+  load_batch(0);
+  const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
+  const int npart = len > 0 ? (len + p.Lc - 1) / p.Lc : 0;
   float M = -INFINITY, W = 0.f, acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
@@ -36,14 +54,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     }
   }
   for (int cb = 0; cb < npart; cb += NB) {
-    float le[NB], o[NB][CPL];
+    if (cb > 0) load_batch(cb);
+    // chunks past the request's end hold stale values: weight 0, value 0
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const bool ok = cb + i < npart;    // the same for every lane
-      le[i] = ok ? p.part_lse[base + cb + i] : -INFINITY;
-      const float* op = p.part_o + (base + cb + i) * D + c0l;
+      const bool ok = cb + i < npart;
+      le[i] = ok ? u2f(__builtin_amdgcn_readlane(f2u(lel), i)) : -INFINITY;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) o[i][c] = ok ? op[c] : 0.f;
+      for (int c = 0; c < CPL; ++c) o[i][c] = ok ? o[i][c] : 0.f;
     }
     float mb = M;
 #pragma unroll
