@@ -368,3 +368,35 @@ def test_per_step_coding_runs_on_the_same_kernels():
         o, lse = layer.decode(t, q, ref_cache[t - 1], bt, lens)
         ref = ref_decode(cfg, t, q, ref_cache[t - 1], bt, lens, cb)
         assert compare(cfg, o, lse, ref, lens)[1] <= 1.0
+
+
+def test_combine_ignores_stale_partials():
+    # The combine loads a whole batch of chunk partials before it knows the
+    # request's own chunk count, then drops the chunks past that count.  With
+    # every workspace byte set to 0xff beforehand (NaN in each partial the
+    # split does not write), the short requests' outputs must still match the
+    # oracle, and an empty request must give zeros and lse = -inf.
+    cfg = synth.config_by_name("layer1p4b").replace(H_kv=4, H_q=4)
+    lens = np.array([4096, 3, 0, 130, 2047, 64])
+    bt, npg, caches = _random_cache_case(cfg, lens, 17)
+    cb = synth.make_codebooks(cfg.replace(n_calib=300))
+    layer = GpuLayer(cfg, cb, int(lens.max()))
+    B, msl = len(lens), int(lens.max())
+    q = synth.make_queries(cfg, B, t=2)
+    ws = torch.full((lv.loopvq_decode_workspace_bytes(layer.dims, B, msl),), 0xff, dtype=torch.uint8,
+                    device="cuda")
+    out = torch.empty((B, cfg.H_q, cfg.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device="cuda")
+    bt_d, seq_d = to_dev(bt.astype(np.int32)), to_dev(lens.astype(np.int32))
+    lv.loopvq_decode_split(layer.dims, 2, io_tensor(cfg, q), to_dev(caches[0]), layer.slices, layer.rope, bt_d,
+                           seq_d, msl, ws, max_pos=layer.max_pos)
+    lv.loopvq_decode_combine(layer.dims, B, seq_d, msl, ws, out, lse)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o)), "a stale partial reached the output"
+    assert np.all(o[2] == 0) and np.all(np.isneginf(l[2]))
+    ref = ref_decode(cfg, 2, q, caches[0], bt, lens, cb)
+    err, ratio = compare(cfg, o, l, ref, lens)
+    _note(f"combine over stale partials: max err {err:.2e} (bound ratio {ratio:.2f})")
+    assert ratio <= 1.0
