@@ -285,13 +285,13 @@ def test_split_invariance_determinism_and_edges():
     assert np.all(oz == 0) and np.all(np.isneginf(lz))
 
 
-@pytest.mark.parametrize("page_size", [8, 256])
+@pytest.mark.parametrize("page_size", [8, 256, 1024])   # 1024: the largest page size the boundary takes
 def test_page_sizes(page_size):
     cfg = synth.config_by_name("layer1p4b").replace(page_size=page_size, H_kv=4, H_q=4)
-    lens = np.array([600, 37])
+    lens = np.array([1500, 37])                # with 1024-token pages: one full page and a partial one
     bt, npg, caches = _random_cache_case(cfg, lens, 21)
     cb = synth.make_codebooks(cfg.replace(n_calib=300))
-    layer = GpuLayer(cfg, cb, 600)
+    layer = GpuLayer(cfg, cb, 1500)
     q = synth.make_queries(cfg, 2, t=3)
     o, lse = layer.decode(3, q, caches[0], bt, lens)
     ref = ref_decode(cfg, 3, q, caches[0], bt, lens, cb)
